@@ -1,0 +1,141 @@
+"""Seeded synthetic workloads for exact attention: shapes, dtypes and input recipes.
+
+This module holds no attention arithmetic.  It only draws Q, K, V (and dO) from a
+seeded CPU generator and rounds them to the storage dtype, so that the HIP path
+and the fp64 CPU checker receive bit-identical inputs.
+
+Workloads (B, H, N, d, storage dtype, causal):
+
+* ``single_head_f32``      1, 1,   256,  64, fp32, no   -- forward only, O and LSE.
+* ``prefill_bf16``         1, 8,  4096,  64, bf16, yes  -- 4,096-token, 8-head prefill.
+* ``gpt2_medium_train``   16, 16, 1024,  64, bf16, yes  -- forward + backward, dO ~ N(0,1).
+* ``long_f16``             4, 16, 8192,  64, fp16, no   -- naive S would be 8.59 GB.
+* ``long_bf16``            1, 16, 16384, 64, bf16, no
+* ``large_head_causal``    2, 16, 8192, 128, bf16, yes  -- forward + backward; in Q and K,
+  for each (b, h) independently, round(0.05 N) row indices drawn without replacement
+  are scaled by 8 (exact in bf16) to stress the running-max rescaling.
+* ``smoke_2x4x512``        2, 4,   512,  64, bf16, no   -- the consistency smoke test
+  shape and seed 0 from the cf-1.com article, section 3.3.
+
+Recipe: each tensor is drawn i.i.d. N(0, 1) in fp32 on the CPU with
+``torch.Generator().manual_seed(seed)`` and cast (round-to-nearest-even) to the storage
+dtype.  Seeds are ``seed_base + t`` with t = 1 (Q), 2 (K), 3 (V), 4 (dO), 5 (Q outlier
+rows), 6 (K outlier rows).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "torch_dtype", "elem_bytes", "fwd_flops", "bwd_flops"]
+
+_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def torch_dtype(name: str) -> torch.dtype:
+    return _DTYPES[name]
+
+
+def elem_bytes(name: str) -> int:
+    return {"f32": 4, "f16": 2, "bf16": 2}[name]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str
+    causal: bool
+    backward: bool
+    seed_base: int
+    outlier_frac: float = 0.0
+    outlier_scale: float = 1.0
+    note: str = field(default="", compare=False)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def shape(self):
+        return (self.B, self.H, self.N, self.d)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("single_head_f32", 1, 1, 256, 64, "f32", False, False, 1000),
+        Workload("prefill_bf16", 1, 8, 4096, 64, "bf16", True, False, 2000),
+        Workload("gpt2_medium_train", 16, 16, 1024, 64, "bf16", True, True, 3000),
+        Workload("long_f16", 4, 16, 8192, 64, "f16", False, False, 41000),
+        Workload("long_bf16", 1, 16, 16384, 64, "bf16", False, False, 42000),
+        Workload("large_head_causal", 2, 16, 8192, 128, "bf16", True, True, 5000, 0.05, 8.0),
+        Workload("smoke_2x4x512", 2, 4, 512, 64, "bf16", False, False, 0),
+    ]
+}
+
+
+def _randn(shape, seed: int) -> torch.Tensor:
+    g = torch.Generator().manual_seed(int(seed))
+    return torch.randn(*shape, generator=g, dtype=torch.float32)
+
+
+def _scale_rows(x: torch.Tensor, frac: float, factor: float, seed: int) -> torch.Tensor:
+    """Scale round(frac*N) rows of every (b, h) slice of x by ``factor``."""
+    B, H, N, _ = x.shape
+    count = int(round(frac * N))
+    if count == 0:
+        return x
+    g = torch.Generator().manual_seed(int(seed))
+    x = x.clone()
+    for b in range(B):
+        for h in range(H):
+            rows = torch.randperm(N, generator=g)[:count]
+            x[b, h, rows] *= factor
+    return x
+
+
+def make_inputs(B: int, H: int, N: int, d: int, dtype: str, seed_base: int,
+                outlier_frac: float = 0.0, outlier_scale: float = 1.0, with_do: bool = False):
+    """Return dict of CPU tensors q, k, v (and do) in the storage dtype.
+
+    Shapes are (B, H, N, d), contiguous.  Values are N(0,1) fp32 draws rounded to the
+    storage dtype; with ``outlier_frac`` the chosen Q and K rows are multiplied by
+    ``outlier_scale`` before rounding (a power of two, so the product is exact).
+    """
+    shape = (B, H, N, d)
+    td = torch_dtype(dtype)
+    q = _randn(shape, seed_base + 1)
+    k = _randn(shape, seed_base + 2)
+    v = _randn(shape, seed_base + 3)
+    if outlier_frac > 0:
+        q = _scale_rows(q, outlier_frac, outlier_scale, seed_base + 5)
+        k = _scale_rows(k, outlier_frac, outlier_scale, seed_base + 6)
+    out = {"q": q.to(td).contiguous(), "k": k.to(td).contiguous(), "v": v.to(td).contiguous()}
+    if with_do:
+        out["do"] = _randn(shape, seed_base + 4).to(td).contiguous()
+    return out
+
+
+def workload_inputs(w: Workload, with_do: bool | None = None):
+    """Inputs of a named workload at its full size."""
+    return make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed_base, w.outlier_frac, w.outlier_scale,
+                       with_do=w.backward if with_do is None else with_do)
+
+
+def fwd_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
+    """Forward work convention: 4 B H N^2 d (two N x N x d products), halved for causal."""
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def bwd_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:
+    """Backward work convention: 10 B H N^2 d (five N x N x d products, including the
+    recomputation of S), halved for causal."""
+    f = 10.0 * B * H * N * N * d
+    return f / 2 if causal else f

@@ -1,0 +1,248 @@
+"""Pins for the fp64 oracle, written as functions of the implementation under test.
+
+Each pin takes callables ``fwd(q, k, v, scale, causal) -> (O, LSE)`` and/or
+``bwd(q, k, v, dO, scale, causal) -> (dQ, dK, dV)`` for one head (2-D arrays) and
+raises AssertionError when the implementation disagrees with something the pages
+or the mathematics fix.  ``test_oracle_pins.py`` runs them on the oracle;
+``test_oracle_mutants.py`` runs them on copies of the oracle with a planted mistake
+and checks that some pin fails.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- forward pins
+
+
+def pin_worked_softmax(fwd):
+    """Softmax of [2, 1, 3] embedded in an attention head: q0 = e1, k_j = x_j e1,
+    v_j = e_(j+1), scale 1.  Row 0 of O is the softmax weights; exp(LSE_0) is the sum."""
+    g = golden("softmax_2_1_3.json")
+    x = np.array(g["row"])
+    n, d = 3, 4
+    q = np.zeros((n, d)); q[:, 0] = 1.0
+    k = np.zeros((n, d)); k[:, 0] = x
+    v = np.zeros((n, d)); v[np.arange(n), np.arange(n) + 1] = 1.0
+    o, lse = fwd(q, k, v, 1.0, False)
+    np.testing.assert_array_equal(np.round(o[0, 1:4], g["weights_decimals"]), g["weights"])
+    assert o[0, 0] == 0.0
+    assert round(float(np.exp(lse[0])), g["sum_decimals"]) == g["sum"]
+    # each exponential: weight * sum
+    np.testing.assert_array_equal(np.round(o[0, 1:4] * np.exp(lse[0]), g["exp_decimals"]), g["exp"])
+
+
+def pin_worked_two_block(fwd):
+    """[1, 2, 0, 3] as the score row of query 0: the direct normaliser with m = 3 is the
+    value the two-block example reaches, 1.553, so LSE_0 = 3 + ln(1.553...)."""
+    g = golden("online_two_block.json")
+    x = np.array(g["row"])
+    n, d = 4, 2
+    q = np.zeros((n, d)); q[:, 0] = 1.0
+    k = np.zeros((n, d)); k[:, 0] = x
+    v = np.zeros((n, d)); v[:, 1] = np.arange(n)
+    _, lse = fwd(q, k, v, 1.0, False)
+    m = g["after_block_2"]["m"]
+    assert round(float(np.exp(lse[0] - m)), g["decimals"]) == g["after_block_2"]["l"]
+
+
+def pin_overflow(fwd):
+    """Scores far beyond the fp32 exp limit stay finite: a row [1000, 999] gives weights
+    e/(e+1) and 1/(e+1) (closed form)."""
+    g = golden("fp32_exp_limit.json")
+    with np.errstate(over="ignore"):
+        assert np.isinf(np.float32(np.exp(np.float32(g["overflow_exponent"]))))
+    assert round(math.log(np.finfo(np.float32).max), g["limit_decimals"]) == g["limit_exponent"]
+    q = np.array([[1.0, 0.0], [1.0, 0.0]])
+    k = np.array([[1000.0, 0.0], [999.0, 0.0]])
+    v = np.array([[1.0, 0.0], [0.0, 1.0]])
+    o, lse = fwd(q, k, v, 1.0, False)
+    w = math.e / (math.e + 1.0)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    np.testing.assert_allclose(o[0], [w, 1.0 - w], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0], 1000.0 + math.log1p(math.exp(-1.0)), rtol=1e-15, atol=0)
+
+
+def pin_q_zero(fwd, causal):
+    """Q = 0: every visible key has the same score, so O_i is the mean of the visible
+    V rows and LSE_i = ln(number of visible keys)."""
+    r = _rng(11)
+    n, d = 9, 5
+    q = np.zeros((n, d)); k = r.standard_normal((n, d)); v = r.standard_normal((n, d))
+    o, lse = fwd(q, k, v, 0.3, causal)
+    for i in range(n):
+        vis = i + 1 if causal else n
+        np.testing.assert_allclose(o[i], v[:vis].mean(axis=0), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse[i], math.log(vis), rtol=0, atol=1e-13)
+
+
+def pin_single_key(fwd):
+    """N = 1: O = V and LSE = scale q.k."""
+    r = _rng(12)
+    q, k, v = (r.standard_normal((1, 7)) for _ in range(3))
+    o, lse = fwd(q, k, v, 0.7, True)
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse[0], 0.7 * float(q[0] @ k[0]), rtol=1e-14, atol=1e-14)
+
+
+def pin_constant_v(fwd, causal):
+    """All V rows equal c: O_i = c for every row."""
+    r = _rng(13)
+    n, d = 8, 6
+    q, k = r.standard_normal((n, d)), r.standard_normal((n, d))
+    c = r.standard_normal(d)
+    o, _ = fwd(q, k, np.tile(c, (n, 1)), 0.5, causal)
+    np.testing.assert_allclose(o, np.tile(c, (n, 1)), rtol=0, atol=1e-13)
+
+
+def pin_key_shift(fwd, causal):
+    """K_j -> K_j + u for every key: each score row moves by a constant, so O is
+    unchanged and LSE_i moves by scale q_i.u."""
+    r = _rng(14)
+    n, d = 10, 4
+    q, k, v = (r.standard_normal((n, d)) for _ in range(3))
+    u = r.standard_normal(d)
+    o1, l1 = fwd(q, k, v, 0.4, causal)
+    o2, l2 = fwd(q, k + u, v, 0.4, causal)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2, l1 + 0.4 * (q @ u), rtol=0, atol=1e-12)
+
+
+def pin_rows_sum_to_one(fwd, causal):
+    """P rows sum to 1 and, with causal masking, vanish above the diagonal: with V = I,
+    O = P."""
+    r = _rng(15)
+    n = 7
+    q, k = r.standard_normal((n, 3)), r.standard_normal((n, 3))
+    p, _ = fwd(q, k, np.eye(n), 0.9, causal)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    assert np.all(p >= 0)
+    if causal:
+        assert np.all(np.triu(p, 1) == 0.0)
+        assert np.all(np.diag(p) > 0)
+
+
+def pin_sdpa(fwd, causal, n=33, d=16, seed=16):
+    """torch's scaled_dot_product_attention (CPU, float64, math path) as an
+    independent library routine; LSE against torch.logsumexp of the masked scores."""
+    r = _rng(seed)
+    q, k, v = (r.standard_normal((n, d)) for _ in range(3))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fwd(q, k, v, scale, causal)
+    tq, tk, tv = (torch.from_numpy(a)[None, None] for a in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)[0, 0]
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+    s = torch.from_numpy(q) @ torch.from_numpy(k).T * scale
+    if causal:
+        s = s.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- backward pins
+
+
+def pin_autograd(bwd, causal, n=21, d=8, seed=17):
+    """Gradients of torch's fp64 SDPA (autograd on CPU) against the oracle's."""
+    r = _rng(seed)
+    q, k, v, do = (r.standard_normal((n, d)) for _ in range(4))
+    scale = 1.0 / math.sqrt(d)
+    tq, tk, tv = (torch.from_numpy(a)[None, None].requires_grad_(True) for a in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale)
+    out.backward(torch.from_numpy(do)[None, None])
+    dq, dk, dv = bwd(q, k, v, do, scale, causal)
+    np.testing.assert_allclose(dq, tq.grad[0, 0].numpy(), rtol=0, atol=1e-10)
+    np.testing.assert_allclose(dk, tk.grad[0, 0].numpy(), rtol=0, atol=1e-10)
+    np.testing.assert_allclose(dv, tv.grad[0, 0].numpy(), rtol=0, atol=1e-10)
+
+
+def pin_finite_differences(fwd, bwd, causal, n=6, d=3, seed=18):
+    """Central differences of L = sum(O * dO) against dQ, dK, dV at every entry."""
+    r = _rng(seed)
+    q, k, v, do = (r.standard_normal((n, d)) for _ in range(4))
+    scale = 0.8
+    dq, dk, dv = bwd(q, k, v, do, scale, causal)
+    h = 1e-6
+
+    def loss(qq, kk, vv):
+        return float(np.sum(fwd(qq, kk, vv, scale, causal)[0] * do))
+
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = xp, xm
+            num[idx] = (loss(args_p["q"], args_p["k"], args_p["v"]) - loss(args_m["q"], args_m["k"], args_m["v"])) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=0, atol=1e-7, err_msg=f"d{name}")
+
+
+def pin_backward_invariants(bwd, causal, n=12, d=5, seed=19):
+    """sum_j dK_j = 0 (rows of dS sum to zero); sum_j dV_j = sum_i dO_i (rows of P sum
+    to one); with causal masking dQ_0 = 0 (row 0 sees only key 0)."""
+    r = _rng(seed)
+    q, k, v, do = (r.standard_normal((n, d)) for _ in range(4))
+    dq, dk, dv = bwd(q, k, v, do, 0.6, causal)
+    np.testing.assert_allclose(dk.sum(axis=0), 0.0, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv.sum(axis=0), do.sum(axis=0), rtol=0, atol=1e-12)
+    if causal:
+        np.testing.assert_allclose(dq[0], 0.0, rtol=0, atol=1e-14)
+
+
+def pin_backward_scaling(bwd, causal, n=9, d=4, seed=20):
+    """(Q, scale) -> (aQ, scale/a) leaves S unchanged: dK and dV unchanged, dQ -> dQ/a;
+    K -> K + u leaves dQ, dK, dV unchanged."""
+    r = _rng(seed)
+    q, k, v, do = (r.standard_normal((n, d)) for _ in range(4))
+    a = 2.5
+    g1 = bwd(q, k, v, do, 0.5, causal)
+    g2 = bwd(a * q, k, v, do, 0.5 / a, causal)
+    np.testing.assert_allclose(g2[0] * a, g1[0], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(g2[1], g1[1], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(g2[2], g1[2], rtol=0, atol=1e-12)
+    u = r.standard_normal(d)
+    g3 = bwd(q, k + u, v, do, 0.5, causal)
+    for x, y in zip(g3, g1):
+        np.testing.assert_allclose(x, y, rtol=0, atol=1e-12)
+
+
+FORWARD_PINS = [
+    ("worked_softmax", lambda f: pin_worked_softmax(f)),
+    ("worked_two_block", lambda f: pin_worked_two_block(f)),
+    ("overflow", lambda f: pin_overflow(f)),
+    ("single_key", lambda f: pin_single_key(f)),
+] + [
+    (f"{name}_{'causal' if c else 'full'}", (lambda p, c: (lambda f: p(f, c)))(p, c))
+    for name, p in (("q_zero", pin_q_zero), ("constant_v", pin_constant_v), ("key_shift", pin_key_shift),
+                    ("rows_sum_to_one", pin_rows_sum_to_one), ("sdpa", pin_sdpa))
+    for c in (False, True)
+]
+
+BACKWARD_PINS = [
+    (f"{name}_{'causal' if c else 'full'}", (lambda p, c: (lambda f, b: p(b, c)))(p, c))
+    for name, p in (("autograd", pin_autograd), ("invariants", pin_backward_invariants),
+                    ("scaling", pin_backward_scaling))
+    for c in (False, True)
+] + [
+    (f"finite_differences_{'causal' if c else 'full'}", (lambda c: (lambda f, b: pin_finite_differences(f, b, c)))(c))
+    for c in (False, True)
+]
