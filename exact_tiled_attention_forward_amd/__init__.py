@@ -1,0 +1,139 @@
+"""Exact tiled attention for AMD Instinct MI355X (gfx950): Python binding of libfa.so.
+
+The work runs in HIP kernels behind a C ABI (``include/fa.h``).  This module only
+marshals arguments: it checks that tensors live on the GPU, are contiguous and agree in
+shape and dtype, allocates outputs with torch when the caller passes none, and calls the
+library on torch's current stream.  There is no other code path: if ``libfa.so`` is
+missing, every call raises.
+
+    import torch, exact_tiled_attention_forward_amd as fa
+    o, lse = fa.fa_forward(q, k, v, causal=True)              # (B, H, N, d) bf16/fp16/fp32
+    dq, dk, dv = fa.fa_backward(q, k, v, o, do, lse, causal=True)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # the HIP runtime torch loads is the one libfa.so binds to (same soname)
+
+__all__ = ["fa_forward", "fa_backward", "fa_backward_workspace_bytes", "library", "FAError",
+           "FA_F32", "FA_F16", "FA_BF16", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    """A non-zero status from the C ABI."""
+
+    def __init__(self, status: int, text: str):
+        super().__init__(f"fa status {status}: {text}")
+        self.status = status
+
+
+def library() -> ctypes.CDLL:
+    """Load libfa.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m exact_tiled_attention_forward_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+    lib.fa_forward.restype = i
+    lib.fa_backward_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_backward_workspace_bytes.restype = sz
+    lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
+    lib.fa_backward.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = i
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise FAError(status, library().fa_status_string(status).decode())
+
+
+def _gpu_tensor(name, t, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def fa_forward(q, k, v, o=None, lse=None, *, scale=None, causal=False, stream=None):
+    """O, lse = attention(q, k, v); tensors (B, H, N, d), lse (B, H, N) float32."""
+    lib = library()
+    if q.dim() != 4:
+        raise ValueError("q must be (B, H, N, d)")
+    B, H, N, d = q.shape
+    dt = q.dtype
+    if dt not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {dt}")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    pq = _gpu_tensor("q", q, dt)
+    pk = _gpu_tensor("k", k, dt, q.shape)
+    pv = _gpu_tensor("v", v, dt, q.shape)
+    po = _gpu_tensor("o", o, dt, q.shape)
+    pl = _gpu_tensor("lse", lse, torch.float32, (B, H, N))
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib.fa_forward(pq, pk, pv, po, pl, B, H, N, d, ctypes.c_float(sc), int(bool(causal)),
+                          _DTYPE_CODE[dt], _stream(stream, q.device)))
+    return o, lse
+
+
+def fa_backward_workspace_bytes(B, H, N, d):
+    return int(library().fa_backward_workspace_bytes(B, H, N, d))
+
+
+def fa_backward(q, k, v, o, do, lse, dq=None, dk=None, dv=None, *, scale=None, causal=False,
+                workspace=None, stream=None):
+    """dQ, dK, dV (float32, (B, H, N, d)) of sum(O * dO), recomputing P from q, k and lse."""
+    lib = library()
+    B, H, N, d = q.shape
+    dt = q.dtype
+    if dt not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {dt}")
+    f32 = torch.float32
+    dq = torch.empty(q.shape, dtype=f32, device=q.device) if dq is None else dq
+    dk = torch.empty(q.shape, dtype=f32, device=q.device) if dk is None else dk
+    dv = torch.empty(q.shape, dtype=f32, device=q.device) if dv is None else dv
+    need = fa_backward_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    ptrs = [_gpu_tensor("q", q, dt), _gpu_tensor("k", k, dt, q.shape), _gpu_tensor("v", v, dt, q.shape),
+            _gpu_tensor("o", o, dt, q.shape), _gpu_tensor("do", do, dt, q.shape),
+            _gpu_tensor("lse", lse, f32, (B, H, N)), _gpu_tensor("dq", dq, f32, q.shape),
+            _gpu_tensor("dk", dk, f32, q.shape), _gpu_tensor("dv", dv, f32, q.shape),
+            _gpu_tensor("workspace", workspace)]
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib.fa_backward(*ptrs, workspace.numel() * workspace.element_size(), B, H, N, d,
+                           ctypes.c_float(sc), int(bool(causal)), _DTYPE_CODE[dt], _stream(stream, q.device)))
+    return dq, dk, dv

@@ -1,0 +1,107 @@
+// C ABI of the attention library: argument validation, then dispatch to the kernels.
+// Every check runs before any HIP call, so a rejected call touches no device state.
+#include "fa.h"
+
+#include <math.h>
+#include <stdint.h>
+
+#include "fa_launch.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int elem_size(int dtype) {
+  switch (dtype) {
+    case FA_F32: return 4;
+    case FA_F16: return 2;
+    case FA_BF16: return 2;
+    default: return 0;
+  }
+}
+
+// Shape checks shared by forward and backward.
+int check_shape(int B, int H, int N, int d, int dtype) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  const int es = elem_size(dtype);
+  if (es == 0) return FA_ERR_UNSUPPORTED;
+  // one head of a tensor addressed with 32-bit byte offsets (fp32 gradients: 4 bytes)
+  if ((int64_t)N * d * 4 >= (int64_t)1 << 31) return FA_ERR_SHAPE;
+  // grid: B*H*ceil(N/32) workgroups at most
+  const int64_t groups = (int64_t)B * H * ((N + 31) / 32);
+  if (groups >= (int64_t)1 << 31) return FA_ERR_SHAPE;
+  if ((int64_t)B * H >= (int64_t)1 << 30) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+int check_scale(float scale) {
+  if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, fa_dtype_t dtype, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d, (int)dtype);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse)) return FA_ERR_ALIGN;
+
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal != 0, (int)dtype, stream};
+  (void)hipGetLastError();  // clear a pending error so the check below is about this launch
+  if (fa::launch_forward(a) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
+  (void)d;
+  if (B < 1 || H < 1 || N < 1) return 0;
+  return (size_t)B * H * N * sizeof(float);
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes, int B, int H, int N,
+                int d, float scale, int causal, fa_dtype_t dtype, hipStream_t stream) {
+  if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  int st = check_shape(B, H, N, d, (int)dtype);
+  if (st != FA_OK) return st;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned4(lse))
+    return FA_ERR_ALIGN;
+  if (!workspace || workspace_bytes < fa_backward_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+
+  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, (float*)workspace, B, H, N, d, scale, causal != 0, (int)dtype,
+                stream};
+  (void)hipGetLastError();
+  if (fa::launch_backward(a) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "B, H or N < 1, or a tensor is too large for the kernels' 32-bit offsets";
+    case FA_ERR_UNSUPPORTED: return "unsupported head dimension (d must be 64 or 128), dtype, or fp32 backward";
+    case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned (lse: 4-byte)";
+    case FA_ERR_WORKSPACE: return "backward workspace is NULL or smaller than fa_backward_workspace_bytes()";
+    case FA_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    case FA_ERR_SCALE: return "scale must be finite and > 0";
+    default: return "unknown status";
+  }
+}
+
+int fa_version(void) { return kVersion; }
+
+}  // extern "C"

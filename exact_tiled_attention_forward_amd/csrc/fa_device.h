@@ -1,0 +1,194 @@
+// Device building blocks for the gfx950 (CDNA4) attention kernels.
+//
+// Conventions used by every kernel in this library
+// ------------------------------------------------
+// * Matrix core: v_mfma_f32_32x32x16_{bf16,f16}, wave64.  For C[32x32] += A[32x16] B[16x32]
+//   lane l holds A[l%32][8*(l/32) + j] and B[8*(l/32) + j][l%32] (j = 0..7, 16-bit values),
+//   and C[8*(i/4) + 4*(l/32) + i%4][l%32] in accumulator register i = 0..15.
+//   Any permutation of the contraction index that both operands share leaves C unchanged;
+//   the kernels use this to feed a C tile straight back as the next product's operand.
+// * Tiles in LDS are row-major [row][col] 16-bit, D columns (D = 64 or 128), with the
+//   16-byte chunks of each row permuted by an XOR swizzle (swz below).  The swizzle is
+//   chosen so that both access patterns the kernels use are free of bank conflicts:
+//     - row reads: 16 consecutive lanes read the same chunk of 16 consecutive rows
+//       (ds_read_b128, an MFMA operand whose contraction index runs along the row);
+//     - transposing reads: a 32-lane half wave reads 4 consecutive rows x 4 consecutive
+//       chunks (ds_read_b64_tr_b16, an operand whose contraction index runs down the
+//       columns).
+//   Tiles are filled by buffer_load ... lds (direct HBM -> LDS, 16 bytes per lane): a wave
+//   instruction writes 1 KiB of LDS contiguously, and the swizzle is applied by choosing
+//   which global chunk each lane fetches.  Rows past the end of the sequence fall outside
+//   the buffer resource's range and arrive as zeros.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit dwords (gfx9 family)
+
+// ------------------------------------------------------------------ 16-bit element types
+
+struct bf16_t {
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // two fp32 -> two bf16 (round to nearest even), packed low/high
+  static __device__ __forceinline__ uint32_t pack(float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
+  }
+  static __device__ __forceinline__ float to_f32(uint16_t u) {
+    return __uint_as_float(((uint32_t)u) << 16);
+  }
+  // acc + lo + hi of a packed pair, in one v_dot2 against (1, 1)
+  static __device__ __forceinline__ float sum2(uint32_t packed, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed),
+                                           __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+  }
+};
+
+struct f16_t {
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack(float x, float y) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, f16x2));
+  }
+  static __device__ __forceinline__ float to_f32(uint16_t u) {
+    return (float)__builtin_bit_cast(_Float16, u);
+  }
+  static __device__ __forceinline__ float sum2(uint32_t packed, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), __builtin_bit_cast(f16x2, 0x3c003c00u), acc,
+                                  false);
+  }
+};
+
+// ------------------------------------------------------------------ swizzled tiles
+
+// XOR applied to the 16-byte chunk index of row r of a D-column 16-bit tile.
+//  D = 128 (16 chunks = 256 B per row, a full bank sweep): f(r) = 4*(r%4) + (r/4)%4.
+//  D = 64  (8 chunks = 128 B per row, two rows per bank sweep): f(r) = 4*((r/2)%2) + (r/4)%4.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(D == 64 || D == 128, "head dim");
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// Byte offset in a swizzled tile of the 16-byte chunk c of row r.
+template <int D>
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return r * (D * 2) + ((c ^ swz<D>(r)) << 4);
+}
+
+// Row read: this lane's 8 consecutive 16-bit values (one chunk) of row r.
+template <int D>
+__device__ __forceinline__ u32x4 lds_row16(const FA_LDS uint8_t* tile, int r, int c) {
+  return *(const FA_LDS u32x4*)(tile + tile_off<D>(r, c));
+}
+
+// Transposing read (ds_read_b64_tr_b16).  Within each 16-lane group, lane i names row
+// r(i) and the 4 columns col0(i)..col0(i)+3; the hardware returns to lane i the column
+// (group base + i) of the 4x16 block formed by lanes 4e..4e+3 (e = 0..3) -> 4 values, one
+// per row r(4e + ...).  Here each lane passes its own row and column (col multiple of 4).
+template <int D>
+__device__ __forceinline__ u32x2 lds_tr16(const FA_LDS uint8_t* tile, int r, int col) {
+  const int off = r * (D * 2) + ((((col >> 3) ^ swz<D>(r)) << 4) | ((col & 7) << 1));
+  i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(tile + off));
+  return __builtin_bit_cast(u32x2, t);
+}
+
+// MFMA operand with the contraction index running down the columns of a tile:
+// lane l gets rows {rbase + 4*(l/32) + e, rbase + 8 + 4*(l/32) + e : e = 0..3} of column
+// cbase + l%32.  This matches the row order of an accumulator tile's registers 8m..8m+7
+// (rows 16m + 8*(j/4) + 4*(l/32) + j%4), so an accumulator C tile converted to 16-bit can
+// be paired with it directly.
+template <int D>
+__device__ __forceinline__ u32x4 lds_colop(const FA_LDS uint8_t* tile, int rbase, int cbase, int lane) {
+  const int i = lane & 15;
+  const int g = lane >> 4;              // 0..3
+  const int h = g >> 1;                 // lane / 32
+  const int r = rbase + 4 * h + (i >> 2);
+  const int col = cbase + 16 * (g & 1) + 4 * (i & 3);
+  u32x2 lo = lds_tr16<D>(tile, r, col);
+  u32x2 hi = lds_tr16<D>(tile, r + 8, col);
+  return (u32x4){lo.x, lo.y, hi.x, hi.y};
+}
+
+// Fill `rows` x D tile (16-bit) from global rows [row0, row0 + rows) of a head whose
+// buffer resource covers exactly that head.  NT threads cooperate; each wave instruction
+// moves 1 KiB.  Out-of-range rows read as zeros.
+template <int D, int ROWS, int NT>
+__device__ __forceinline__ void tile_load_async(FA_LDS uint8_t* tile, __amdgpu_buffer_rsrc_t rs, int row0, int tid) {
+  constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  constexpr int CHUNKS = ROWS * CPR;
+  constexpr int PER_INSTR = 64;
+  constexpr int WAVES = NT / 64;
+  static_assert(CHUNKS % (PER_INSTR * WAVES) == 0, "tile must split evenly over waves");
+  const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int t = 0; t < CHUNKS / (PER_INSTR * WAVES); ++t) {
+    const int base = (t * WAVES + wave) * PER_INSTR;   // wave-uniform chunk index
+    const int p = base + lane;
+    const int r = p / CPR;
+    const int slot = p % CPR;
+    const int c = slot ^ swz<D>(r);
+    const int voff = (row0 + r) * (D * 2) + (c << 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)(tile + base * 16), 16, voff, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rs, int voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Value of x held by lane l^32 (the other half of the wave): v_permlane32_swap.
+__device__ __forceinline__ float other_half(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  // lanes 0..31 receive the upper half's value in the second result, lanes 32..63 the
+  // lower half's value in the first result
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Row index (within a 32-row accumulator tile) held in register i by this lane's half.
+__device__ __forceinline__ constexpr int acc_row(int i, int half) {
+  return 8 * (i >> 2) + 4 * half + (i & 3);
+}
+
+}  // namespace fa

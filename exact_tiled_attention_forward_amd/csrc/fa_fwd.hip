@@ -1,0 +1,349 @@
+// Exact attention forward on gfx950: O = softmax(scale * Q K^T) V, one tile at a time.
+//
+// Method ("Flash Attention", mlx.void.app, sections 地基：流式 softmax and
+// FlashAttention-2; "FlashAttention：IO 感知的快速内存高效精确注意力", trdm.cn, section
+// 基准/方法设计): every workgroup owns one (batch, head, query block); it streams the key
+// and value tiles of that head through LDS and keeps, per query row, a running max m, a
+// running sum l and an unnormalised output o.  When a tile raises the max, l and o are
+// multiplied by e^(m_old - m_new); after the last tile O = o / l.  The N x N score
+// matrix never leaves the chip.  The per-row logsumexp m + ln l is written for the
+// backward pass.  With causal masking, tiles that lie wholly in a query's future are
+// not computed (same page, FlashAttention-2 section).
+//
+// Mapping to CDNA4 (one wave = 64 lanes owns 32 query rows):
+//   * S^T = K Q^T on v_mfma_f32_32x32x16: K (A operand) is read row-wise from LDS, Q (B
+//     operand) stays in registers for the whole kernel.  In the accumulator, lane l holds
+//     query l%32 and 16 of the tile's 32 keys, so the row max and row sum are in-lane
+//     reductions plus one v_permlane32_swap between the wave's halves.
+//   * exponentials in base 2: p = exp2(s*c - m) with c = scale*log2(e), one FMA + one
+//     v_exp_f32 per score; m and l live in base 2 and LSE is converted at the end.
+//   * O^T += V^T P^T: P^T is the S^T accumulator converted to 16 bits in place (B
+//     operand); V^T is read from the row-major V tile with ds_read_b64_tr_b16.  Besides
+//     the fp32 row sum l (for the logsumexp), a second sum adds up the 16-bit
+//     probabilities the product actually used (v_dot2 with (1, 1)) and normalises O.
+//   * K/V tiles are fetched HBM -> LDS with buffer_load ... lds, double-buffered, so the
+//     next tile's fetch overlaps this tile's math.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+// ----------------------------------------------------------------------------------
+// 16-bit inputs (bf16 or fp16), fp32 accumulation.
+//   NW waves per workgroup, 32 query rows per wave -> BR = 32*NW rows per workgroup.
+//   BC keys per tile.
+// ----------------------------------------------------------------------------------
+template <class T, int D, int NW, int BC, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void fwd16_kernel(const uint16_t* __restrict__ Q,
+                                                        const uint16_t* __restrict__ K,
+                                                        const uint16_t* __restrict__ V,
+                                                        uint16_t* __restrict__ O, float* __restrict__ LSE,
+                                                        int BH, int N, float c) {
+  constexpr int BR = 32 * NW;
+  constexpr int NT = NW * 64;
+  constexpr int TB = BC * D * 2;  // bytes of one K or V tile
+  constexpr int KB = BC / 32;     // 32-key accumulator blocks per tile
+  constexpr int DS = D / 16;      // contraction steps over the head dimension
+  constexpr int DB = D / 32;      // 32-wide blocks of the output's head dimension
+  static_assert(BC % 32 == 0, "key tile");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TB];  // K0 K1 V0 V1
+  FA_LDS uint8_t* lds = (FA_LDS uint8_t*)(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, c32 = lane & 31;
+  const int nqb = (N + BR - 1) / BR;
+  const int bh = blockIdx.x % BH;
+  int qb = blockIdx.x / BH;
+  if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
+  const int q0 = qb * BR;
+  const int qw0 = q0 + 32 * wave;
+  const int qrow = qw0 + c32;
+
+  const size_t head = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const auto rq = make_rsrc(Q + head, head_bytes);
+  const auto rk = make_rsrc(K + head, head_bytes);
+  const auto rv = make_rsrc(V + head, head_bytes);
+
+  const int nkt_all = (N + BC - 1) / BC;
+  const int nkt = CAUSAL ? min(nkt_all, (q0 + BR - 1) / BC + 1) : nkt_all;
+
+  tile_load_async<D, BC, NT>(lds, rk, 0, tid);
+  tile_load_async<D, BC, NT>(lds + 2 * TB, rv, 0, tid);
+
+  u32x4 qf[DS];
+#pragma unroll
+  for (int st = 0; st < DS; ++st) qf[st] = buffer_load16(rq, qrow * (D * 2) + ((2 * st + half) << 4));
+
+  // base-2 running max m (of s*c); this half's running sums: l of the fp32 probabilities
+  // (for the logsumexp) and lr of the same probabilities rounded to 16 bits (for O)
+  float m = -INFINITY, l = 0.f, lr = 0.f;
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
+
+  for (int j = 0; j < nkt; ++j) {
+    wait_vmem();
+    __syncthreads();
+    const int cur = j & 1;
+    if (j + 1 < nkt) {
+      tile_load_async<D, BC, NT>(lds + (cur ^ 1) * TB, rk, (j + 1) * BC, tid);
+      tile_load_async<D, BC, NT>(lds + (2 + (cur ^ 1)) * TB, rv, (j + 1) * BC, tid);
+    }
+    const int k0 = j * BC;
+    if (CAUSAL && k0 > qw0 + 31) continue;  // every key of the tile is in this wave's future
+    const FA_LDS uint8_t* kt = lds + cur * TB;
+    const FA_LDS uint8_t* vt = lds + (2 + cur) * TB;
+
+    // S^T = K Q^T for the tile
+    f32x16 s[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = (f32x16){};
+#pragma unroll
+      for (int st = 0; st < DS; ++st) s[kb] = T::mfma(lds_row16<D>(kt, 32 * kb + c32, 2 * st + half), qf[st], s[kb]);
+    }
+
+    // masks: keys past the end, and (causal) keys after the query
+    if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw0)) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + 32 * kb + acc_row(i, half);
+          if (key >= N || (CAUSAL && key > qrow)) s[kb][i] = -INFINITY;
+        }
+    }
+
+    // online softmax: new running max, rescale factor, exponentials
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = max_halves(mx);
+    const float m_new = fmaxf(m, mx * c);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    float rs = 0.f, rsr = 0.f;
+    uint32_t pk[KB][8];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float p0 = fast_exp2(fmaf(s[kb][2 * t], c, -m_use));
+        const float p1 = fast_exp2(fmaf(s[kb][2 * t + 1], c, -m_use));
+        rs += p0 + p1;
+        pk[kb][t] = T::pack(p0, p1);
+        rsr = T::sum2(pk[kb][t], rsr);
+      }
+    l = l * alpha + rs;
+    lr = lr * alpha + rsr;
+    m = m_new;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int ks = 0; ks < BC / 16; ++ks) {
+      const int kb = ks >> 1, mm = ks & 1;
+      const u32x4 b = (u32x4){pk[kb][4 * mm], pk[kb][4 * mm + 1], pk[kb][4 * mm + 2], pk[kb][4 * mm + 3]};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = T::mfma(lds_colop<D>(vt, 16 * ks, 32 * db, lane), b, o[db]);
+    }
+  }
+
+  // epilogue: one division per row, 16-bit O, natural-log LSE.  O divides by the sum of
+  // the rounded probabilities the P V product used, which makes it an exact weighted
+  // average of V rows; the logsumexp uses the fp32 sum.
+  const float lt = sum_halves(l);
+  const float inv = 1.0f / sum_halves(lr);
+  if (qrow < N) {
+    uint16_t* orow = O + head + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * half;
+        u32x2 w;
+        w.x = T::pack(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+        w.y = T::pack(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+        *(u32x2*)(orow + d) = w;
+      }
+    if (half == 0) LSE[(size_t)bh * N + qrow] = (m + log2f(lt)) * kLn2;
+  }
+}
+
+// ----------------------------------------------------------------------------------
+// fp32 inputs: the same schedule on v_mfma_f32_32x32x2_f32 (fp32 in, fp32 accumulate).
+// Tiles go through registers into padded LDS rows (K stride D+2, V stride D+8 floats),
+// which keeps both operand reads free of bank conflicts.
+// ----------------------------------------------------------------------------------
+template <int D, int NW, int BC, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                        const float* __restrict__ V, float* __restrict__ O,
+                                                        float* __restrict__ LSE, int BH, int N, float c) {
+  constexpr int BR = 32 * NW;
+  constexpr int NT = NW * 64;
+  constexpr int KS = D + 2, VS = D + 8;
+  constexpr int KB = BC / 32;
+  constexpr int DB = D / 32;
+  __shared__ __attribute__((aligned(16))) float ks_[BC * KS];
+  __shared__ __attribute__((aligned(16))) float vs_[BC * VS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, c32 = lane & 31;
+  const int nqb = (N + BR - 1) / BR;
+  const int bh = blockIdx.x % BH;
+  int qb = blockIdx.x / BH;
+  if (CAUSAL) qb = nqb - 1 - qb;
+  const int q0 = qb * BR;
+  const int qw0 = q0 + 32 * wave;
+  const int qrow = qw0 + c32;
+  const size_t head = (size_t)bh * N * D;
+  const auto rq = make_rsrc(Q + head, (uint32_t)N * D * 4);
+  const auto rk = make_rsrc(K + head, (uint32_t)N * D * 4);
+  const auto rv = make_rsrc(V + head, (uint32_t)N * D * 4);
+
+  float qv[D / 2];  // this lane's query at d = 2*st + half
+#pragma unroll
+  for (int st = 0; st < D / 8; ++st) {
+    // 4 consecutive floats d = 8*st' + 4*? are not what the operand needs; load the
+    // pairs (2*st4 + half) for st4 in 4 steps: d = 8*st + 2*e + half, e = 0..3
+    const u32x4 w0 = buffer_load16(rq, qrow * D * 4 + (8 * st) * 4);
+    const u32x4 w1 = buffer_load16(rq, qrow * D * 4 + (8 * st + 4) * 4);
+    const float f[8] = {__uint_as_float(w0.x), __uint_as_float(w0.y), __uint_as_float(w0.z), __uint_as_float(w0.w),
+                        __uint_as_float(w1.x), __uint_as_float(w1.y), __uint_as_float(w1.z), __uint_as_float(w1.w)};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qv[4 * st + e] = half ? f[2 * e + 1] : f[2 * e];
+  }
+
+  const int nkt_all = (N + BC - 1) / BC;
+  const int nkt = CAUSAL ? min(nkt_all, (q0 + BR - 1) / BC + 1) : nkt_all;
+  float m = -INFINITY, l = 0.f;
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
+
+  for (int j = 0; j < nkt; ++j) {
+    const int k0 = j * BC;
+    __syncthreads();  // previous tile fully consumed
+    constexpr int V4 = BC * D / 4;  // float4 chunks per tile
+    for (int p = tid; p < V4; p += NT) {
+      const int r = p / (D / 4), cc = (p % (D / 4)) * 4;
+      const u32x4 kw = buffer_load16(rk, (k0 + r) * D * 4 + cc * 4);
+      const u32x4 vw = buffer_load16(rv, (k0 + r) * D * 4 + cc * 4);
+      float* kd = ks_ + r * KS + cc;
+      *(f32x2*)kd = (f32x2){__uint_as_float(kw.x), __uint_as_float(kw.y)};
+      *(f32x2*)(kd + 2) = (f32x2){__uint_as_float(kw.z), __uint_as_float(kw.w)};
+      *(u32x4*)(vs_ + r * VS + cc) = vw;
+    }
+    __syncthreads();
+    if (CAUSAL && k0 > qw0 + 31) continue;
+
+    f32x16 s[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = (f32x16){};
+#pragma unroll
+      for (int st = 0; st < D / 2; ++st)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(ks_[(32 * kb + c32) * KS + 2 * st + half], qv[st], s[kb], 0, 0, 0);
+    }
+    if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw0)) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + 32 * kb + acc_row(i, half);
+          if (key >= N || (CAUSAL && key > qrow)) s[kb][i] = -INFINITY;
+        }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = max_halves(mx);
+    const float m_new = fmaxf(m, mx * c);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[kb][i] = fast_exp2(fmaf(s[kb][i], c, -m_use));
+        rs += s[kb][i];
+      }
+    l = l * alpha + rs;
+    m = m_new;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = 32 * kb + acc_row(i, half);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vs_[key * VS + 32 * db + c32], s[kb][i], o[db], 0, 0, 0);
+      }
+  }
+
+  const float lt = sum_halves(l);
+  const float inv = 1.0f / lt;
+  if (qrow < N) {
+    float* orow = O + head + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * half;
+        *(f32x4*)(orow + d) = (f32x4){o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
+                                      o[db][4 * g + 3] * inv};
+      }
+    if (half == 0) LSE[(size_t)bh * N + qrow] = (m + log2f(lt)) * kLn2;
+  }
+}
+
+// ----------------------------------------------------------------------------------
+// launchers
+// ----------------------------------------------------------------------------------
+namespace {
+constexpr int kNW16 = 4, kBC16 = 64;
+constexpr int kNW32 = 2, kBC32 = 32;
+
+template <class T, int D, bool CAUSAL>
+hipError_t go16(const FwdArgs& a) {
+  constexpr int BR = 32 * kNW16;
+  const int nqb = (a.N + BR - 1) / BR;
+  hipLaunchKernelGGL((fwd16_kernel<T, D, kNW16, kBC16, CAUSAL>), dim3(a.B * a.H * nqb), dim3(kNW16 * 64), 0, a.stream,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
+                     a.B * a.H, a.N, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t go32(const FwdArgs& a) {
+  constexpr int BR = 32 * kNW32;
+  const int nqb = (a.N + BR - 1) / BR;
+  hipLaunchKernelGGL((fwd32_kernel<D, kNW32, kBC32, CAUSAL>), dim3(a.B * a.H * nqb), dim3(kNW32 * 64), 0, a.stream,
+                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.B * a.H, a.N,
+                     a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t by_dtype(const FwdArgs& a) {
+  switch (a.dtype) {
+    case kDtypeBF16: return a.causal ? go16<bf16_t, D, true>(a) : go16<bf16_t, D, false>(a);
+    case kDtypeF16: return a.causal ? go16<f16_t, D, true>(a) : go16<f16_t, D, false>(a);
+    case kDtypeF32: return a.causal ? go32<D, true>(a) : go32<D, false>(a);
+  }
+  return hipErrorInvalidValue;
+}
+}  // namespace
+
+hipError_t launch_forward(const FwdArgs& a) {
+  return a.d == 64 ? by_dtype<64>(a) : by_dtype<128>(a);
+}
+
+}  // namespace fa

@@ -1,0 +1,48 @@
+// Internal launch interface between the C ABI (fa_api.cpp) and the kernels.
+// Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+
+namespace fa {
+
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeF16 = 1;
+constexpr int kDtypeBF16 = 2;
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, N, d;
+  float scale;
+  bool causal;
+  int dtype;
+  hipStream_t stream;
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dO;
+  const float* lse;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* delta;  // workspace: D_i = dO_i . O_i, B*H*N floats
+  int B, H, N, d;
+  float scale;
+  bool causal;
+  int dtype;
+  hipStream_t stream;
+};
+
+hipError_t launch_forward(const FwdArgs& a);
+hipError_t launch_backward(const BwdArgs& a);
+
+}  // namespace fa

@@ -1,0 +1,130 @@
+/*
+ * fa.h -- exact tiled attention on AMD Instinct MI355X (gfx950), C ABI.
+ *
+ * The library computes exact softmax attention, O = softmax(scale * Q K^T) V, one tile at
+ * a time with the online-softmax rescaling (running max m, running sum l, unnormalised
+ * output o), so the N x N score matrix is never written to device memory, and its
+ * gradient by recomputing the score tiles from Q, K and the saved per-row logsumexp.
+ *
+ * Where the operations are defined (page title, section):
+ *   - "Flash Attention" (mlx.void.app, chapter 4 deep-dive): intro (the same
+ *     softmax(QK^T/sqrt(d)) V, exact up to rounding order); 地基：流式 softmax (safe and
+ *     online softmax, the e^(old max - new max) patch); FlashAttention——把整件事分块塞进
+ *     SRAM (tiles, recomputation from the saved (m, l) in the backward pass);
+ *     FlashAttention-2 (query blocks across the grid, one division by l at the end,
+ *     skipping fully masked causal blocks).
+ *   - "FlashAttention：IO 感知的快速内存高效精确注意力" (NeurIPS 2022 summary, trdm.cn):
+ *     基准/方法设计 (tiling and the (m, l) merge rule), 方法细节 (backward recomputation,
+ *     kernel fusion, correctness theorem).
+ *   - "大模型数学速成（17）：Flash Attention——不物化注意力矩阵" (shiguol.github.io):
+ *     二 (S = QK^T/sqrt(d), P = softmax(S), O = PV), 三 (tiles + online softmax).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *   Layout    Q, K, V, O, dO, dQ, dK, dV are contiguous row-major (B, H, N, d) tensors:
+ *             element (b, h, i, c) is at ((b*H + h)*N + i)*d + c.  lse and the
+ *             backward workspace are (B, H, N) float.
+ *   dtype     q, k, v, o and dO share one storage type, fa_dtype_t.  Arithmetic is
+ *             fp32 (products of 16-bit inputs accumulate in fp32; the probabilities are
+ *             rounded to the input type before the P V product).
+ *   scale     multiplies Q K^T; callers normally pass 1/sqrt(d).  Must be finite and > 0.
+ *   causal    non-zero: key j is visible to query i only if j <= i (diagonal included).
+ *   lse       natural-log logsumexp of each scaled, masked score row:
+ *             lse_i = m_i + ln(l_i), the pages' saved statistics (m, l) in one number.
+ *   memory    all pointers are device pointers the caller allocated (e.g. with
+ *             hipMalloc or a framework's allocator); the library allocates nothing,
+ *             keeps no state between calls, and never frees caller memory.
+ *   async     work is enqueued on `stream` (0 = the null stream) and the call returns
+ *             without waiting.  Faults inside a kernel surface at the caller's next
+ *             synchronisation, not as a return code.
+ *   errors    every argument is checked before anything is enqueued; a failing check
+ *             returns a negative fa_status_t and enqueues nothing.  FA_ERR_HIP means
+ *             the HIP runtime rejected a launch (hipGetLastError after the launch; the
+ *             runtime's pending error is cleared before launching).
+ *   threads   entry points are stateless and may be called from several host threads.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_F32 = 0,  /* IEEE fp32 storage (forward only) */
+  FA_F16 = 1,  /* IEEE fp16 storage */
+  FA_BF16 = 2  /* bfloat16 storage */
+} fa_dtype_t;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = -2,       /* B, H or N < 1, or a (B, H, N, d) tensor too large */
+  FA_ERR_UNSUPPORTED = -3, /* d not in {64, 128}, unknown dtype, or fp32 backward */
+  FA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned */
+  FA_ERR_WORKSPACE = -5,   /* backward workspace NULL or smaller than required */
+  FA_ERR_HIP = -6,         /* the HIP runtime rejected a kernel launch */
+  FA_ERR_SCALE = -7        /* scale is not finite or not > 0 */
+} fa_status_t;
+
+/*
+ * Largest N for head dimension d and element size s (bytes): one (b, h) slice of a
+ * tensor, N*d*s bytes, must stay below 2^31 (the kernels address within a head with
+ * 32-bit offsets).  B*H*ceil(N/32) must also fit a grid dimension.
+ */
+
+/*
+ * fa_forward -- O and lse for one attention call.
+ *   q, k, v  in : (B, H, N, d) of `dtype`.
+ *   o        out: (B, H, N, d) of `dtype`, O_i = sum_j P_ij V_j with
+ *                 P = softmax(scale * Q K^T) (causal-masked if `causal`).
+ *   lse      out: (B, H, N) float, lse_i = ln sum_j exp(scale * q_i . k_j) over visible j.
+ *   B, H, N  batch, heads, sequence length (>= 1; any N, no padding needed).
+ *   d        head dimension, 64 or 128.
+ * Returns FA_OK or a negative fa_status_t (nothing enqueued on error).
+ * o and lse must not overlap the inputs.
+ */
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal,
+               fa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * fa_backward_workspace_bytes -- bytes of device workspace fa_backward needs:
+ * 4*B*H*N (one float D_i = dO_i . O_i per query row).  Returns 0 if B, H or N < 1.
+ */
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * fa_backward -- gradients of sum(O * dO) with respect to Q, K and V.
+ *   q, k, v, o, dO  in : (B, H, N, d) of `dtype` (fp16 or bf16); o is the forward
+ *                        output for the same q, k, v, scale and causal.
+ *   lse             in : (B, H, N) float from fa_forward for the same call.
+ *   dq, dk, dv      out: (B, H, N, d) float (fp32 gradients).
+ *   workspace       scratch of at least fa_backward_workspace_bytes(B, H, N, d) bytes,
+ *                   16-byte aligned; its contents on entry are ignored.
+ * The score tiles are recomputed from Q, K and lse ("FlashAttention：IO 感知…",
+ * 方法细节; "Flash Attention", FlashAttention section on training): with
+ * P = exp(scale*QK^T - lse), dV = P^T dO, dP = dO V^T, D_i = dO_i . O_i,
+ * dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
+ * The result is deterministic (no atomics).  Returns FA_OK or a negative fa_status_t.
+ */
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                const float* lse, float* dq, float* dk, float* dv,
+                void* workspace, size_t workspace_bytes,
+                int B, int H, int N, int d, float scale, int causal,
+                fa_dtype_t dtype, hipStream_t stream);
+
+/* fa_status_string -- static, human-readable text for a status code. */
+const char* fa_status_string(int status);
+
+/* fa_version -- library version as major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

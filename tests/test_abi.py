@@ -1,0 +1,127 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and rejects
+bad arguments with the documented status before touching the device.
+
+No call here passes a complete set of valid arguments, so nothing is ever launched.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_forward_amd as fa
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "fa.h")
+
+FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_SCALE = (
+    0, -1, -2, -3, -4, -5, -6, -7)
+
+needs_lib = pytest.mark.skipif(not os.path.exists(fa.LIB_PATH), reason="libfa.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("fa_forward", "fa_backward", "fa_backward_workspace_bytes", "fa_status_string", "fa_version"):
+        assert required in names
+
+
+@needs_lib
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fa.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in fa.h but not exported"
+
+
+@needs_lib
+def test_status_strings_and_version():
+    lib = fa.library()
+    for st in (FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_HIP,
+               FA_ERR_SCALE):
+        s = lib.fa_status_string(st).decode()
+        assert s and s != "unknown status"
+    assert lib.fa_status_string(12345).decode() == "unknown status"
+    assert lib.fa_version() >= 100
+
+
+P = ctypes.c_void_p(0x10000)   # aligned, never dereferenced: every call below fails validation
+P2 = ctypes.c_void_p(0x20000)
+MIS = ctypes.c_void_p(0x10008)
+NUL = ctypes.c_void_p(0)
+
+
+def fwd(q=P, k=P, v=P, o=P2, lse=P2, B=1, H=1, N=16, d=64, scale=0.125, causal=0, dtype=fa.FA_BF16):
+    return fa.library().fa_forward(q, k, v, o, lse, B, H, N, d, ctypes.c_float(scale), causal, dtype, NUL)
+
+
+def bwd(ptrs=None, ws=P2, wsb=1 << 20, B=1, H=1, N=16, d=64, scale=0.125, dtype=fa.FA_BF16):
+    ptrs = ptrs or [P] * 9
+    return fa.library().fa_backward(*ptrs, ws, wsb, B, H, N, d, ctypes.c_float(scale), 0, dtype, NUL)
+
+
+@needs_lib
+@pytest.mark.parametrize("which", range(5))
+def test_forward_null(which):
+    args = [P, P, P, P2, P2]
+    args[which] = NUL
+    assert fwd(*args, d=96) == FA_ERR_NULL  # null wins over every other error
+
+
+@needs_lib
+def test_forward_shape_and_dtype_errors():
+    assert fwd(B=0, d=96) == FA_ERR_SHAPE
+    assert fwd(H=-1, d=96) == FA_ERR_SHAPE
+    assert fwd(N=0, d=96) == FA_ERR_SHAPE
+    assert fwd(d=96) == FA_ERR_UNSUPPORTED
+    assert fwd(d=32) == FA_ERR_UNSUPPORTED
+    assert fwd(d=64, dtype=7) == FA_ERR_UNSUPPORTED
+    assert fwd(N=1 << 23, d=128, scale=-1.0) == FA_ERR_SHAPE       # a head of 2^31 fp32 bytes
+    assert fwd(B=1 << 16, H=1 << 14, N=64, scale=-1.0) == FA_ERR_SHAPE
+
+
+@needs_lib
+def test_forward_scale_and_alignment_errors():
+    assert fwd(scale=0.0) == FA_ERR_SCALE
+    assert fwd(scale=-0.5) == FA_ERR_SCALE
+    assert fwd(scale=float("inf")) == FA_ERR_SCALE
+    assert fwd(scale=float("nan")) == FA_ERR_SCALE
+    for i in range(4):
+        args = [P, P, P, P2, ctypes.c_void_p(0x20002)]
+        args[i] = MIS
+        assert fwd(*args) == FA_ERR_ALIGN
+    assert fwd(lse=ctypes.c_void_p(0x20002)) == FA_ERR_ALIGN
+
+
+@needs_lib
+def test_backward_errors():
+    lib = fa.library()
+    assert lib.fa_backward_workspace_bytes(2, 3, 5, 64) == 2 * 3 * 5 * 4
+    assert lib.fa_backward_workspace_bytes(0, 3, 5, 64) == 0
+    for i in range(9):
+        ptrs = [P] * 9
+        ptrs[i] = NUL
+        assert bwd(ptrs, d=96) == FA_ERR_NULL
+    assert bwd(d=96) == FA_ERR_UNSUPPORTED
+    assert bwd(N=0) == FA_ERR_SHAPE
+    assert bwd(dtype=fa.FA_F32) == FA_ERR_UNSUPPORTED
+    assert bwd(scale=0.0) == FA_ERR_SCALE
+    ptrs = [P] * 9
+    ptrs[6] = MIS
+    assert bwd(ptrs) == FA_ERR_ALIGN
+    assert bwd(ws=NUL) == FA_ERR_WORKSPACE
+    assert bwd(wsb=16 * 4 - 1) == FA_ERR_WORKSPACE
+    assert bwd(ws=ctypes.c_void_p(0x20004), wsb=64) == FA_ERR_ALIGN
+
+
+@needs_lib
+def test_python_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_forward(q, q, q)
