@@ -64,7 +64,7 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
   (void)d;
   if (B < 1 || H < 1 || N < 1) return 0;
-  return (size_t)B * H * N * sizeof(float);
+  return (size_t)2 * B * H * N * sizeof(float);  // D_i, then lse_i * log2(e)
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,

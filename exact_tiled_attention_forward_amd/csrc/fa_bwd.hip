@@ -1,6 +1,371 @@
-// placeholder until the backward kernels land
+// Exact attention backward on gfx950, recomputing the score tiles instead of storing P.
+//
+// Method ("Flash Attention", mlx.void.app, FlashAttention section on training: only O and
+// the per-row statistics are kept and the score tiles are rebuilt from Q and K on chip;
+// "FlashAttention：IO 感知的快速内存高效精确注意力", trdm.cn, 方法细节: backward
+// recomputation as selective checkpointing).  With the saved logsumexp lse the
+// probabilities come back in one step, P = exp(scale*QK^T - lse), with no running max.
+// The gradient formulas are the calculus of O = softmax(S) V (the pages give none):
+//   dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij,  dS = P * (dP - D),
+//   dQ = scale dS K,  dK = scale dS^T Q.
+//
+// Accuracy choices (the gradients must hold an absolute error bar at magnitudes ~30):
+//   * D_i is summed from the recomputed fp32 P and dP, not as dO_i . O_i from the stored
+//     16-bit O, whose rounding (and the forward's 16-bit P) would otherwise reach the
+//     gradients amplified by sum_j P_ij K_j.
+//   * P and dS enter the dV, dK and dQ products as a 16-bit pair hi + lo (split2), two
+//     MFMAs against the exactly representable Q, K or dO operand.
+//
+// Two kernels on the caller's stream, deterministic (no atomics):
+//   1. dq:    one workgroup per (batch, head, block of 32*NW queries), Q and dO in
+//             registers, K and V tiles streamed through LDS twice.  Pass 1: S^T = K Q^T,
+//             dP^T = V dO^T, D_i = sum_j P_ij dP_ij.  Pass 2: the same tiles again,
+//             dS^T = P^T (dP^T - D), dQ^T += K^T dS^T (K^T by ds_read_b64_tr_b16).
+//             Writes D and lse*log2(e) to the workspace for kernel 2.
+//   2. dkdv:  one workgroup per (batch, head, block of 32*NW keys), K and V in
+//             registers, Q and dO tiles (and their D, lse) streamed through LDS.
+//             S = Q K^T, dP = dO V^T (lane = key), then dV^T += dO^T P and
+//             dK^T += Q^T dS with dO^T / Q^T from transposing LDS reads.
 #include "fa_device.h"
 #include "fa_launch.h"
+
 namespace fa {
-hipError_t launch_backward(const BwdArgs&) { return hipErrorNotSupported; }
+
+// ----------------------------------------------------------------------------------
+// 1. dQ (and D, lse2).  NW waves x 32 queries per workgroup; BC keys per tile.
+// ----------------------------------------------------------------------------------
+template <class T, int D, int NW, int BC, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                         const uint16_t* __restrict__ V,
+                                                         const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
+                                                         float* __restrict__ delta, float* __restrict__ lse2,
+                                                         float* __restrict__ dQ, int BH, int N, float c, float scale) {
+  constexpr int BR = 32 * NW;
+  constexpr int NT = NW * 64;
+  constexpr int TB = BC * D * 2;
+  constexpr int KB = BC / 32;
+  constexpr int DS = D / 16;
+  constexpr int DB = D / 32;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TB];  // K0 K1 V0 V1
+  FA_LDS uint8_t* lds = (FA_LDS uint8_t*)(smem);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, c32 = lane & 31;
+  const int nqb = (N + BR - 1) / BR;
+  const int bh = blockIdx.x % BH;
+  int qb = blockIdx.x / BH;
+  if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
+  const int q0 = qb * BR;
+  const int qw0 = q0 + 32 * wave;
+  const int qrow = qw0 + c32;
+
+  const size_t head = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const auto rq = make_rsrc(Q + head, head_bytes);
+  const auto rk = make_rsrc(K + head, head_bytes);
+  const auto rv = make_rsrc(V + head, head_bytes);
+  const auto rdo = make_rsrc(dO + head, head_bytes);
+
+  const int nkt_all = (N + BC - 1) / BC;
+  const int nkt = CAUSAL ? min(nkt_all, (q0 + BR - 1) / BC + 1) : nkt_all;
+
+  u32x4 qf[DS], of[DS];
+#pragma unroll
+  for (int st = 0; st < DS; ++st) {
+    qf[st] = buffer_load16(rq, qrow * (D * 2) + ((2 * st + half) << 4));
+    of[st] = buffer_load16(rdo, qrow * (D * 2) + ((2 * st + half) << 4));
+  }
+  const bool qvalid = qrow < N;
+  const float l2 = qvalid ? LSE[(size_t)bh * N + qrow] * kLog2e : 0.f;
+
+  float dsum = 0.f;  // pass 1: this half's part of D_i = sum_j P_ij dP_ij
+  float dl = 0.f;    // pass 2: D_i
+  f32x16 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dq[db] = (f32x16){};
+
+  for (int pass = 0; pass < 2; ++pass) {
+    __syncthreads();  // the previous pass is done with both LDS buffers
+    tile_load_async<D, BC, NT>(lds, rk, 0, tid);
+    tile_load_async<D, BC, NT>(lds + 2 * TB, rv, 0, tid);
+    for (int j = 0; j < nkt; ++j) {
+      wait_vmem();
+      __syncthreads();
+      const int cur = j & 1;
+      if (j + 1 < nkt) {
+        tile_load_async<D, BC, NT>(lds + (cur ^ 1) * TB, rk, (j + 1) * BC, tid);
+        tile_load_async<D, BC, NT>(lds + (2 + (cur ^ 1)) * TB, rv, (j + 1) * BC, tid);
+      }
+      const int k0 = j * BC;
+      if (CAUSAL && k0 > qw0 + 31) continue;
+      const FA_LDS uint8_t* kt = lds + cur * TB;
+      const FA_LDS uint8_t* vt = lds + (2 + cur) * TB;
+      const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw0);
+
+      uint32_t sh[KB][8], sl[KB][8];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        f32x16 s = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+        for (int st = 0; st < DS; ++st) {
+          s = T::mfma(lds_row16<D>(kt, 32 * kb + c32, 2 * st + half), qf[st], s);
+          dp = T::mfma(lds_row16<D>(vt, 32 * kb + c32, 2 * st + half), of[st], dp);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float p = fast_exp2(fmaf(s[i], c, -l2));
+          if (need_mask) {
+            const int key = k0 + 32 * kb + acc_row(i, half);
+            if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
+          }
+          if (pass == 0) dsum = fmaf(p, dp[i], dsum);
+          else dp[i] = p * (dp[i] - dl);
+        }
+        if (pass == 1) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) split2<T>(dp[2 * t], dp[2 * t + 1], sh[kb][t], sl[kb][t]);
+        }
+      }
+      if (pass == 1) {
+        // dQ^T += K^T (dS^T hi) + K^T (dS^T lo)
+#pragma unroll
+        for (int ks = 0; ks < BC / 16; ++ks) {
+          const int kb = ks >> 1, mm = ks & 1;
+          const u32x4 bh_ = (u32x4){sh[kb][4 * mm], sh[kb][4 * mm + 1], sh[kb][4 * mm + 2], sh[kb][4 * mm + 3]};
+          const u32x4 bl_ = (u32x4){sl[kb][4 * mm], sl[kb][4 * mm + 1], sl[kb][4 * mm + 2], sl[kb][4 * mm + 3]};
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const u32x4 a = lds_colop<D>(kt, 16 * ks, 32 * db, lane);
+            dq[db] = T::mfma(a, bh_, dq[db]);
+            dq[db] = T::mfma(a, bl_, dq[db]);
+          }
+        }
+      }
+    }
+    if (pass == 0) {
+      dl = sum_halves(dsum);
+      if (qvalid && half == 0) {
+        delta[(size_t)bh * N + qrow] = dl;
+        lse2[(size_t)bh * N + qrow] = l2;
+      }
+    }
+  }
+
+  if (qvalid) {
+    float* dqr = dQ + head + (size_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * half;
+        *(f32x4*)(dqr + d) = (f32x4){dq[db][4 * g] * scale, dq[db][4 * g + 1] * scale, dq[db][4 * g + 2] * scale,
+                                     dq[db][4 * g + 3] * scale};
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------------
+// 2. dK, dV.  NW waves x 32 keys per workgroup; BQ queries per streamed tile.
+// ----------------------------------------------------------------------------------
+template <class T, int D, int NW, int BQ, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                                           const uint16_t* __restrict__ V,
+                                                           const uint16_t* __restrict__ dO,
+                                                           const float* __restrict__ delta,
+                                                           const float* __restrict__ lse2, float* __restrict__ dK,
+                                                           float* __restrict__ dV, int BH, int N, float c,
+                                                           float scale) {
+  constexpr int BKV = 32 * NW;
+  constexpr int NT = NW * 64;
+  constexpr int TB = BQ * D * 2;
+  constexpr int QB = BQ / 32;  // 32-query accumulator blocks per tile
+  constexpr int DS = D / 16;
+  constexpr int DB = D / 32;
+  static_assert(BQ % 32 == 0 && BQ <= 64, "query tile");
+  // Q0 Q1 dO0 dO1, then [buffer][lse2 | delta][64 floats]: a dword DMA instruction
+  // writes all 64 lanes, so each array gets a full 64-float slot
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TB + 2 * 2 * 64 * 4];
+  FA_LDS uint8_t* lds = (FA_LDS uint8_t*)(smem);
+  FA_LDS float* stats = (FA_LDS float*)(smem + 4 * TB);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, c32 = lane & 31;
+  const int bh = blockIdx.x % BH;
+  const int kblk = blockIdx.x / BH;  // causal: block 0 sees the most queries and starts first
+  const int k0 = kblk * BKV;
+  const int kw0 = k0 + 32 * wave;
+  const int krow = kw0 + c32;
+
+  const size_t head = (size_t)bh * N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const auto rq = make_rsrc(Q + head, head_bytes);
+  const auto rk = make_rsrc(K + head, head_bytes);
+  const auto rv = make_rsrc(V + head, head_bytes);
+  const auto rdo = make_rsrc(dO + head, head_bytes);
+  const auto rl = make_rsrc(lse2 + (size_t)bh * N, (uint32_t)N * 4);
+  const auto rd = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4);
+
+  const int nqt = (N + BQ - 1) / BQ;
+  const int qt0 = CAUSAL ? (k0 / BQ) : 0;  // earlier query tiles see none of these keys
+
+  auto load_tile = [&](int qt, int buf) {
+    tile_load_async<D, BQ, NT>(lds + buf * TB, rq, qt * BQ, tid);
+    tile_load_async<D, BQ, NT>(lds + (2 + buf) * TB, rdo, qt * BQ, tid);
+    if (wave == 0) {
+      // 64 floats of lse2 and of delta from the tile's first query (the first BQ used)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (FA_LDS void*)(stats + buf * 128), 4, (qt * BQ + lane) * 4, 0,
+                                               0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (FA_LDS void*)(stats + buf * 128 + 64), 4,
+                                               (qt * BQ + lane) * 4, 0, 0, 0);
+    }
+  };
+
+  if (qt0 < nqt) load_tile(qt0, 0);
+
+  // this wave's keys and values as B operands (lane = key, 8 consecutive d per lane)
+  u32x4 kf[DS], vf[DS];
+#pragma unroll
+  for (int st = 0; st < DS; ++st) {
+    kf[st] = buffer_load16(rk, krow * (D * 2) + ((2 * st + half) << 4));
+    vf[st] = buffer_load16(rv, krow * (D * 2) + ((2 * st + half) << 4));
+  }
+
+  f32x16 dk[DB], dv[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dk[db] = (f32x16){};
+    dv[db] = (f32x16){};
+  }
+
+  for (int qt = qt0; qt < nqt; ++qt) {
+    wait_vmem();
+    __syncthreads();
+    const int cur = (qt - qt0) & 1;
+    if (qt + 1 < nqt) load_tile(qt + 1, cur ^ 1);
+    const int q0 = qt * BQ;
+    if (CAUSAL && q0 + BQ - 1 < kw0) continue;  // every query of the tile precedes this wave's keys
+    const FA_LDS uint8_t* qtile = lds + cur * TB;
+    const FA_LDS uint8_t* otile = lds + (2 + cur) * TB;
+    const FA_LDS float* l2 = stats + cur * 128;
+    const FA_LDS float* dl = l2 + 64;
+    const bool need_mask = (q0 + BQ > N) || (CAUSAL && q0 < kw0 + 31);
+
+    uint32_t ph[QB][8], pl[QB][8], sh[QB][8], sl[QB][8];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      f32x16 s = (f32x16){}, dp = (f32x16){};
+#pragma unroll
+      for (int st = 0; st < DS; ++st) {
+        s = T::mfma(lds_row16<D>(qtile, 32 * qb + c32, 2 * st + half), kf[st], s);
+        dp = T::mfma(lds_row16<D>(otile, 32 * qb + c32, 2 * st + half), vf[st], dp);
+      }
+      // rows of this accumulator: queries q0 + 32*qb + acc_row(i, half)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int r0 = 32 * qb + 8 * a + 4 * half;
+        const f32x4 lv = *(const FA_LDS f32x4*)(l2 + r0);
+        const f32x4 dlv = *(const FA_LDS f32x4*)(dl + r0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * a + e;
+          float p = fast_exp2(fmaf(s[i], c, -lv[e]));
+          if (need_mask) {
+            const int q = q0 + r0 + e;
+            if (q >= N || (CAUSAL && krow > q)) p = 0.f;
+          }
+          s[i] = p;
+          dp[i] = p * (dp[i] - dlv[e]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        split2<T>(s[2 * t], s[2 * t + 1], ph[qb][t], pl[qb][t]);
+        split2<T>(dp[2 * t], dp[2 * t + 1], sh[qb][t], sl[qb][t]);
+      }
+    }
+
+    // dV^T += dO^T (P hi + P lo),  dK^T += Q^T (dS hi + dS lo)
+#pragma unroll
+    for (int ks = 0; ks < BQ / 16; ++ks) {
+      const int qb = ks >> 1, mm = ks & 1;
+      const u32x4 bph = (u32x4){ph[qb][4 * mm], ph[qb][4 * mm + 1], ph[qb][4 * mm + 2], ph[qb][4 * mm + 3]};
+      const u32x4 bpl = (u32x4){pl[qb][4 * mm], pl[qb][4 * mm + 1], pl[qb][4 * mm + 2], pl[qb][4 * mm + 3]};
+      const u32x4 bsh = (u32x4){sh[qb][4 * mm], sh[qb][4 * mm + 1], sh[qb][4 * mm + 2], sh[qb][4 * mm + 3]};
+      const u32x4 bsl = (u32x4){sl[qb][4 * mm], sl[qb][4 * mm + 1], sl[qb][4 * mm + 2], sl[qb][4 * mm + 3]};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const u32x4 ao = lds_colop<D>(otile, 16 * ks, 32 * db, lane);
+        dv[db] = T::mfma(ao, bph, dv[db]);
+        dv[db] = T::mfma(ao, bpl, dv[db]);
+        const u32x4 aq = lds_colop<D>(qtile, 16 * ks, 32 * db, lane);
+        dk[db] = T::mfma(aq, bsh, dk[db]);
+        dk[db] = T::mfma(aq, bsl, dk[db]);
+      }
+    }
+  }
+
+  // lane = key (column of dK^T / dV^T), registers = head-dimension rows
+  if (krow < N) {
+    float* dkr = dK + head + (size_t)krow * D;
+    float* dvr = dV + head + (size_t)krow * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * half;
+        *(f32x4*)(dkr + d) = (f32x4){dk[db][4 * g] * scale, dk[db][4 * g + 1] * scale, dk[db][4 * g + 2] * scale,
+                                     dk[db][4 * g + 3] * scale};
+        *(f32x4*)(dvr + d) = (f32x4){dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------------
+// launchers
+// ----------------------------------------------------------------------------------
+namespace {
+constexpr int kNWkv = 4;
+constexpr int kNWq = 4, kBCq = 64;
+
+template <int D>
+constexpr int bq_for() { return D == 128 ? 32 : 64; }
+
+template <class T, int D, bool CAUSAL>
+hipError_t go(const BwdArgs& a) {
+  const int BH = a.B * a.H;
+  const long rows = (long)BH * a.N;
+  float* delta = a.delta;
+  float* lse2 = a.delta + rows;
+  const float c = a.scale * kLog2e;
+  {
+    constexpr int BR = 32 * kNWq;
+    const int nqb = (a.N + BR - 1) / BR;
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, kNWq, kBCq, CAUSAL>), dim3(BH * nqb), dim3(kNWq * 64), 0, a.stream,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO,
+                       a.lse, delta, lse2, a.dq, BH, a.N, c, a.scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  {
+    constexpr int BKV = 32 * kNWkv;
+    const int nkb = (a.N + BKV - 1) / BKV;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kNWkv, bq_for<D>(), CAUSAL>), dim3(BH * nkb), dim3(kNWkv * 64), 0,
+                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dO, delta, lse2, a.dk, a.dv, BH, a.N, c, a.scale);
+    return hipGetLastError();
+  }
+}
+
+template <int D>
+hipError_t by_dtype(const BwdArgs& a) {
+  switch (a.dtype) {
+    case kDtypeBF16: return a.causal ? go<bf16_t, D, true>(a) : go<bf16_t, D, false>(a);
+    case kDtypeF16: return a.causal ? go<f16_t, D, true>(a) : go<f16_t, D, false>(a);
+  }
+  return hipErrorInvalidValue;
+}
+}  // namespace
+
+hipError_t launch_backward(const BwdArgs& a) {
+  return a.d == 64 ? by_dtype<64>(a) : by_dtype<128>(a);
+}
+
 }  // namespace fa

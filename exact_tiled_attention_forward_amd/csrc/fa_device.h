@@ -62,6 +62,8 @@ struct bf16_t {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed),
                                            __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
   }
+  static __device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
+  static __device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 };
 
 struct f16_t {
@@ -79,7 +81,18 @@ struct f16_t {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), __builtin_bit_cast(f16x2, 0x3c003c00u), acc,
                                   false);
   }
+  static __device__ __forceinline__ float lo_f32(uint32_t w) { return to_f32((uint16_t)(w & 0xffffu)); }
+  static __device__ __forceinline__ float hi_f32(uint32_t w) { return to_f32((uint16_t)(w >> 16)); }
 };
+
+// Two fp32 values as a 16-bit pair hi plus the 16-bit pair of what hi missed, so that
+// hi + lo carries about twice the input type's significand.  A product A (hi + lo),
+// done as two MFMAs, then rounds only what both halves together cannot represent.
+template <class T>
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = T::pack(x0, x1);
+  lo = T::pack(x0 - T::lo_f32(hi), x1 - T::hi_f32(hi));
+}
 
 // ------------------------------------------------------------------ swizzled tiles
 

@@ -34,7 +34,7 @@ struct BwdArgs {
   float* dq;
   float* dk;
   float* dv;
-  float* delta;  // workspace: D_i = dO_i . O_i, B*H*N floats
+  float* delta;  // workspace: D_i = dO_i . O_i (B*H*N floats), then lse_i*log2(e) (B*H*N)
   int B, H, N, d;
   float scale;
   bool causal;

@@ -93,7 +93,8 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * fa_backward_workspace_bytes -- bytes of device workspace fa_backward needs:
- * 4*B*H*N (one float D_i = dO_i . O_i per query row).  Returns 0 if B, H or N < 1.
+ * 8*B*H*N (per query row, D_i = dO_i . O_i and lse_i*log2(e) as floats).  Returns 0 if
+ * B, H or N < 1.
  */
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
 

@@ -101,7 +101,7 @@ def test_forward_scale_and_alignment_errors():
 @needs_lib
 def test_backward_errors():
     lib = fa.library()
-    assert lib.fa_backward_workspace_bytes(2, 3, 5, 64) == 2 * 3 * 5 * 4
+    assert lib.fa_backward_workspace_bytes(2, 3, 5, 64) == 2 * 3 * 5 * 8
     assert lib.fa_backward_workspace_bytes(0, 3, 5, 64) == 0
     for i in range(9):
         ptrs = [P] * 9
@@ -115,8 +115,8 @@ def test_backward_errors():
     ptrs[6] = MIS
     assert bwd(ptrs) == FA_ERR_ALIGN
     assert bwd(ws=NUL) == FA_ERR_WORKSPACE
-    assert bwd(wsb=16 * 4 - 1) == FA_ERR_WORKSPACE
-    assert bwd(ws=ctypes.c_void_p(0x20004), wsb=64) == FA_ERR_ALIGN
+    assert bwd(wsb=16 * 8 - 1) == FA_ERR_WORKSPACE
+    assert bwd(ws=ctypes.c_void_p(0x20004), wsb=128) == FA_ERR_ALIGN
 
 
 @needs_lib

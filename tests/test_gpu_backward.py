@@ -1,0 +1,105 @@
+"""GPU parity of fa_backward (after fa_forward) against the fp64 oracle (needs an MI355X)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import exact_tiled_attention_forward_amd as fa
+from exact_tiled_attention_forward_amd.workloads import WORKLOADS, make_inputs, workload_inputs
+from oracle import naive
+from parity import assert_close, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd_bwd(inp, causal, scale=None):
+    q, k, v, do = (inp[x].cuda() for x in ("q", "k", "v", "do"))
+    o, lse = fa.fa_forward(q, k, v, scale=scale, causal=causal)
+    dq, dk, dv = fa.fa_backward(q, k, v, o, do, lse, scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def check_grads(tag, got, ref, dtype, floor_aware=False):
+    out = []
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        mx, mean, ex, _ = assert_close(f"{tag} {name}", g, r, dtype, out_dtype="f32", floor_aware=floor_aware)
+        out.append(f"{name} max {mx:.2e} mean {mean:.2e}")
+    return "; ".join(out)
+
+
+SMALL_N = [1, 2, 17, 64, 65, 127, 128, 129, 200, 300]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_small_shapes_all_rows(dtype, d, causal):
+    """Ragged N spanning one to several key and query tiles; every gradient entry of
+    every head against the oracle's backward computed from Q, K, V, dO alone."""
+    failures = []
+    for n in SMALL_N:
+        inp = make_inputs(2, 2, n, d, dtype, seed_base=8000 + n, with_do=True)
+        got = run_fwd_bwd(inp, causal)
+        ref = naive.backward(*(to64(inp[x]) for x in ("q", "k", "v", "do")), 1 / math.sqrt(d), causal)
+        for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+            x, r = to64(g), to64(r)
+            e = np.abs(x - r)
+            print(f"{dtype} d={d} causal={causal} N={n} {name}: max {e.max():.2e} mean {e.mean():.2e} "
+                  f"max|ref| {np.abs(r).max():.2e} mean|ref| {np.abs(r).mean():.2e}")
+        try:
+            check_grads(f"N={n}", got, ref, dtype)
+        except AssertionError as exc:
+            failures.append(str(exc))
+    assert not failures, failures
+
+
+def test_backward_alone_from_oracle_statistics():
+    """fa_backward fed the oracle's O (rounded to bf16) and lse rather than the kernel's."""
+    n, d, causal = 257, 64, True
+    inp = make_inputs(1, 3, n, d, "bf16", seed_base=8500, with_do=True)
+    q, k, v, do = (to64(inp[x]) for x in ("q", "k", "v", "do"))
+    o_ref, lse_ref = naive.forward(q, k, v, 1 / math.sqrt(d), causal)
+    tq, tk, tv, tdo = (inp[x].cuda() for x in ("q", "k", "v", "do"))
+    o = torch.from_numpy(o_ref).to(torch.bfloat16).cuda()
+    lse = torch.from_numpy(lse_ref).float().cuda()
+    dq, dk, dv = fa.fa_backward(tq, tk, tv, o, tdo, lse, causal=causal)
+    torch.cuda.synchronize()
+    ref = naive.backward(q, k, v, to64(inp["do"]), 1 / math.sqrt(d), causal)
+    print(check_grads("oracle stats", (dq.cpu(), dk.cpu(), dv.cpu()), ref, "bf16"))
+
+
+def test_backward_deterministic_and_no_writes_past_the_end():
+    B, H, N, d = 1, 3, 333, 128
+    inp = make_inputs(B, H, N, d, "bf16", 9200, with_do=True)
+    q, k, v, do = (inp[x].cuda() for x in ("q", "k", "v", "do"))
+    o, lse = fa.fa_forward(q, k, v, causal=True)
+    sentinel = -7777.0
+    n = B * H * N * d
+    bufs = [torch.full((n + 2048,), sentinel, dtype=torch.float32, device="cuda") for _ in range(3)]
+    grads = [b[:n].view(B, H, N, d) for b in bufs]
+    fa.fa_backward(q, k, v, o, do, lse, *grads, causal=True)
+    first = [g.clone() for g in grads]
+    fa.fa_backward(q, k, v, o, do, lse, *grads, causal=True)
+    torch.cuda.synchronize()
+    for a, b, buf in zip(first, grads, bufs):
+        assert torch.equal(a, b)
+        assert torch.all(buf[n:] == sentinel)
+
+
+@pytest.mark.parametrize("name", ["gpt2_medium_train", "large_head_causal"])
+def test_full_size_sampled_heads(name):
+    """The full forward + backward of the workload; every gradient entry of two sampled
+    heads (the first and the last) against the oracle."""
+    w = WORKLOADS[name]
+    inp = workload_inputs(w)
+    got = run_fwd_bwd(inp, w.causal)
+    for g in got:
+        assert torch.isfinite(g).all()
+    q, k, v, do = (to64(inp[x]) for x in ("q", "k", "v", "do"))
+    for b, h in sorted({(0, 0), (w.B - 1, w.H - 1)}):
+        ref = naive.backward_head(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, w.causal)
+        msg = check_grads(f"[{b},{h}]", tuple(g[b, h] for g in got), ref, w.dtype)
+        print(f"{name} head ({b},{h}): {msg}")
