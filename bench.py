@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""One-GPU benchmark of exact tiled attention (forward + recompute backward) on MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload large_head_causal]
+
+A step is one pass of the whole path over the workload's synthetic inputs, already
+resident in HBM: fa_forward, then the two backward stages (fa_backward_dq,
+fa_backward_dkdv -- exactly what fa_backward runs).  The default workload is causal
+bf16 attention with B=2, H=16, N=8192, d=128 (5% of Q and K rows scaled by 8).
+
+Printed: one JSON line on stdout.  `value` is credited TFLOP/s of the whole step:
+forward 4*B*H*N^2*d and backward 10*B*H*N^2*d (five N x N x d products including the
+recomputation of S), both halved for causal masking.  `roofline` describes the
+kernel with the largest share of the step's time: its algorithmic flops per launch
+over its average launch time, measured here with HIP events on the stream the
+kernels run on, against the MI355X dense bf16 MFMA peak (2516.6 TFLOP/s).
+`cpu_baseline` times the fp64 CPU oracle on a few heads of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16/fp16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+CSRC = os.path.join(ROOT, "exact_tiled_attention_forward_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the HIP/C++ sources of libfa.so (ties stored counter data to a build)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was taken on
+    the current kernel sources; else None."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line:
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    if fields.get("source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def kernel_flops(w):
+    """Credited (algorithmic) flops of each kernel per launch.  The forward kernel owns
+    S = QK^T and O = PV; of the backward's five products the dK/dV kernel owns S, dP,
+    dV and dK, the dQ kernel owns dQ."""
+    unit = 2.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)  # one N x N x d product
+    return {"fwd": 2 * unit, "bwd_dq": 1 * unit, "bwd_dkdv": 4 * unit}
+
+
+def cpu_baseline(w, inp, heads: int):
+    """Time the fp64 oracle (forward + backward) on `heads` heads of the workload."""
+    from oracle import naive
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        blas = [i for i in info if i.get("user_api") == "blas"]
+        cores = int(blas[0]["num_threads"]) if blas else len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        cores = len(os.sched_getaffinity(0))
+    picks = [(b, h) for b in range(w.B) for h in range(w.H)][:heads]
+    arrs = {x: inp[x].double().numpy() for x in ("q", "k", "v", "do") if x in inp}
+    t0 = time.perf_counter()
+    for b, h in picks:
+        naive.forward_head(arrs["q"][b, h], arrs["k"][b, h], arrs["v"][b, h], w.scale, w.causal)
+        if w.backward:
+            naive.backward_head(arrs["q"][b, h], arrs["k"][b, h], arrs["v"][b, h], arrs["do"][b, h], w.scale,
+                                w.causal)
+    secs = time.perf_counter() - t0
+    unit = 2.0 * w.N * w.N * w.d * (0.5 if w.causal else 1.0)  # one N x N x d product of one head
+    per_head = (2 + (5 if w.backward else 0)) * unit
+    return {
+        "value": per_head * len(picks) / secs / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{len(picks)} of {w.B * w.H} heads of {w.name}, fp64 numpy, "
+                  f"{'forward + backward' if w.backward else 'forward'}, {secs:.1f} s",
+        "seconds": secs,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="large_head_causal")
+    ap.add_argument("--cpu-heads", type=int, default=12, help="heads of the CPU oracle sample (0: skip)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        log("bench.py measures one GPU only: attention shards over (batch, head) with no exchange, "
+            "and this library has no multi-GPU path.  Run with --gpus 1.")
+        sys.exit(2)
+
+    import torch
+    import exact_tiled_attention_forward_amd as fa
+    from exact_tiled_attention_forward_amd.workloads import WORKLOADS, workload_inputs
+
+    w = WORKLOADS[args.workload]
+    inp = workload_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    do = inp["do"].to(dev) if w.backward else None
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    if w.backward:
+        f32 = torch.float32
+        dq, dk, dv = (torch.empty(q.shape, dtype=f32, device=dev) for _ in range(3))
+        ws = torch.empty(fa.fa_backward_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    names = ["fwd"] + (["bwd_dq", "bwd_dkdv"] if w.backward else [])
+
+    def step(evs=None):
+        if evs:
+            evs[0].record(stream)
+        fa.fa_forward(q, k, v, o, lse, causal=w.causal, stream=stream)
+        if evs:
+            evs[1].record(stream)
+        if w.backward:
+            fa.fa_backward_dq(q, k, v, do, lse, dq, causal=w.causal, workspace=ws, stream=stream)
+            if evs:
+                evs[2].record(stream)
+            fa.fa_backward_dkdv(q, k, v, do, ws, dk, dv, causal=w.causal, stream=stream)
+            if evs:
+                evs[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    kernel_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, n in enumerate(names)}
+
+    flops = kernel_flops(w)
+    step_flops = sum(flops[n] for n in names)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    dom = max(names, key=lambda n: kernel_ms[n])
+    achieved = flops[dom] / (kernel_ms[dom] * 1e-3) / 1e12
+    fwd_tf = flops["fwd"] / (kernel_ms["fwd"] * 1e-3) / 1e12
+    line = {
+        "metric": "attention fwd/bwd TFLOPS and % of MI355X bf16 MFMA peak, causal N=8192",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded N(0,1) Q, K, V, dO rounded to the storage dtype" +
+                (f"; {w.outlier_frac:.0%} of Q and K rows x{w.outlier_scale:g}" if w.outlier_frac else ""),
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                   "passes": "forward+backward" if w.backward else "forward"},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(fwd_tf, 2),
+        "fwd_pct_of_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2),
+        "kernel_ms": {n: round(t, 4) for n, t in kernel_ms.items()},
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": stored_traffic(dom, w.name),
+        },
+    }
+    if w.backward:
+        bwd_ms = kernel_ms["bwd_dq"] + kernel_ms["bwd_dkdv"]
+        bwd_tf = (flops["bwd_dq"] + flops["bwd_dkdv"]) / (bwd_ms * 1e-3) / 1e12
+        line["bwd_tflops"] = round(bwd_tf, 2)
+        line["bwd_pct_of_peak"] = round(100 * bwd_tf / PEAK_BF16_TFLOPS, 2)
+    log(f"{w.name}: step {ms_per_step:.3f} ms, {value:.1f} TFLOP/s; kernels (ms): "
+        + ", ".join(f"{n} {t:.3f}" for n, t in kernel_ms.items()))
+    if args.cpu_heads > 0:
+        log(f"timing the fp64 CPU oracle on {args.cpu_heads} heads ...")
+        line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -19,8 +19,8 @@ import os
 
 import torch  # the HIP runtime torch loads is the one libfa.so binds to (same soname)
 
-__all__ = ["fa_forward", "fa_backward", "fa_backward_workspace_bytes", "library", "FAError",
-           "FA_F32", "FA_F16", "FA_BF16", "LIB_PATH"]
+__all__ = ["fa_forward", "fa_backward", "fa_backward_dq", "fa_backward_dkdv", "fa_backward_workspace_bytes",
+           "library", "FAError", "FA_F32", "FA_F16", "FA_BF16", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -53,6 +53,10 @@ def library() -> ctypes.CDLL:
     lib.fa_backward_workspace_bytes.restype = sz
     lib.fa_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
     lib.fa_backward.restype = i
+    lib.fa_backward_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
+    lib.fa_backward_dq.restype = i
+    lib.fa_backward_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
+    lib.fa_backward_dkdv.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -137,3 +141,45 @@ def fa_backward(q, k, v, o, do, lse, dq=None, dk=None, dv=None, *, scale=None, c
     _check(lib.fa_backward(*ptrs, workspace.numel() * workspace.element_size(), B, H, N, d,
                            ctypes.c_float(sc), int(bool(causal)), _DTYPE_CODE[dt], _stream(stream, q.device)))
     return dq, dk, dv
+
+
+def _bwd_common(q, workspace):
+    B, H, N, d = q.shape
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    need = fa_backward_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    return B, H, N, d, workspace
+
+
+def fa_backward_dq(q, k, v, do, lse, dq=None, *, scale=None, causal=False, workspace=None, stream=None):
+    """First backward stage: dQ, plus D and lse*log2(e) in ``workspace`` (returned) for
+    fa_backward_dkdv."""
+    lib = library()
+    B, H, N, d, workspace = _bwd_common(q, workspace)
+    dt, f32 = q.dtype, torch.float32
+    dq = torch.empty(q.shape, dtype=f32, device=q.device) if dq is None else dq
+    ptrs = [_gpu_tensor("q", q, dt), _gpu_tensor("k", k, dt, q.shape), _gpu_tensor("v", v, dt, q.shape),
+            _gpu_tensor("do", do, dt, q.shape), _gpu_tensor("lse", lse, f32, (B, H, N)),
+            _gpu_tensor("dq", dq, f32, q.shape), _gpu_tensor("workspace", workspace)]
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib.fa_backward_dq(*ptrs, workspace.numel() * workspace.element_size(), B, H, N, d,
+                              ctypes.c_float(sc), int(bool(causal)), _DTYPE_CODE[dt], _stream(stream, q.device)))
+    return dq, workspace
+
+
+def fa_backward_dkdv(q, k, v, do, workspace, dk=None, dv=None, *, scale=None, causal=False, stream=None):
+    """Second backward stage: dK, dV from the workspace fa_backward_dq filled."""
+    lib = library()
+    B, H, N, d, workspace = _bwd_common(q, workspace)
+    dt, f32 = q.dtype, torch.float32
+    dk = torch.empty(q.shape, dtype=f32, device=q.device) if dk is None else dk
+    dv = torch.empty(q.shape, dtype=f32, device=q.device) if dv is None else dv
+    ptrs = [_gpu_tensor("q", q, dt), _gpu_tensor("k", k, dt, q.shape), _gpu_tensor("v", v, dt, q.shape),
+            _gpu_tensor("do", do, dt, q.shape), _gpu_tensor("dk", dk, f32, q.shape),
+            _gpu_tensor("dv", dv, f32, q.shape), _gpu_tensor("workspace", workspace)]
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib.fa_backward_dkdv(*ptrs, workspace.numel() * workspace.element_size(), B, H, N, d,
+                                ctypes.c_float(sc), int(bool(causal)), _DTYPE_CODE[dt], _stream(stream, q.device)))
+    return dk, dv

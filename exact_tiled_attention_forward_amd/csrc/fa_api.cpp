@@ -67,9 +67,13 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
   return (size_t)2 * B * H * N * sizeof(float);  // D_i, then lse_i * log2(e)
 }
 
-int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
-                float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes, int B, int H, int N,
-                int d, float scale, int causal, fa_dtype_t dtype, hipStream_t stream) {
+namespace {
+
+// Shared checks of the backward entry points; pointers a stage does not use are passed
+// as a valid stand-in (q) by the caller of this helper.
+int check_backward(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                   const float* dq, const float* dk, const float* dv, const void* workspace, size_t workspace_bytes,
+                   int B, int H, int N, int d, float scale, fa_dtype_t dtype) {
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
   int st = check_shape(B, H, N, d, (int)dtype);
   if (st != FA_OK) return st;
@@ -80,12 +84,48 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
     return FA_ERR_ALIGN;
   if (!workspace || workspace_bytes < fa_backward_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
-
-  fa::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, (float*)workspace, B, H, N, d, scale, causal != 0, (int)dtype,
-                stream};
-  (void)hipGetLastError();
-  if (fa::launch_backward(a) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
+}
+
+int run_backward(const void* q, const void* k, const void* v, const void* dO, const float* lse, float* dq,
+                 float* dk, float* dv, void* workspace, int B, int H, int N, int d, float scale, int causal,
+                 fa_dtype_t dtype, hipStream_t stream, int stages) {
+  fa::BwdArgs a{q, k, v, nullptr, dO, lse, dq, dk, dv, (float*)workspace, B, H, N, d, scale, causal != 0,
+                (int)dtype, stream};
+  (void)hipGetLastError();
+  if (fa::launch_backward(a, stages) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+}  // namespace
+
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes, int B, int H, int N,
+                int d, float scale, int causal, fa_dtype_t dtype, hipStream_t stream) {
+  const int st = check_backward(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  return run_backward(q, k, v, dO, lse, dq, dk, dv, workspace, B, H, N, d, scale, causal, dtype, stream,
+                      fa::kStageDq | fa::kStageDkdv);
+}
+
+int fa_backward_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse, float* dq,
+                   void* workspace, size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+                   fa_dtype_t dtype, hipStream_t stream) {
+  const float* f = (const float*)q;  // stand-in for the gradients this stage does not touch
+  const int st = check_backward(q, k, v, q, dO, lse, dq, f, f, workspace, workspace_bytes, B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  return run_backward(q, k, v, dO, lse, dq, nullptr, nullptr, workspace, B, H, N, d, scale, causal, dtype, stream,
+                      fa::kStageDq);
+}
+
+int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dO, float* dk, float* dv,
+                     const void* workspace, size_t workspace_bytes, int B, int H, int N, int d, float scale,
+                     int causal, fa_dtype_t dtype, hipStream_t stream) {
+  const float* f = (const float*)q;
+  const int st = check_backward(q, k, v, q, dO, f, f, dk, dv, workspace, workspace_bytes, B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  return run_backward(q, k, v, dO, nullptr, nullptr, dk, dv, const_cast<void*>(workspace), B, H, N, d, scale,
+                      causal, dtype, stream, fa::kStageDkdv);
 }
 
 const char* fa_status_string(int status) {

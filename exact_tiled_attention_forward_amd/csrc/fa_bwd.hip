@@ -329,13 +329,13 @@ template <int D>
 constexpr int bq_for() { return D == 128 ? 32 : 64; }
 
 template <class T, int D, bool CAUSAL>
-hipError_t go(const BwdArgs& a) {
+hipError_t go(const BwdArgs& a, int stages) {
   const int BH = a.B * a.H;
   const long rows = (long)BH * a.N;
   float* delta = a.delta;
   float* lse2 = a.delta + rows;
   const float c = a.scale * kLog2e;
-  {
+  if (stages & kStageDq) {
     constexpr int BR = 32 * kNWq;
     const int nqb = (a.N + BR - 1) / BR;
     hipLaunchKernelGGL((bwd_dq_kernel<T, D, kNWq, kBCq, CAUSAL>), dim3(BH * nqb), dim3(kNWq * 64), 0, a.stream,
@@ -344,7 +344,7 @@ hipError_t go(const BwdArgs& a) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if (stages & kStageDkdv) {
     constexpr int BKV = 32 * kNWkv;
     const int nkb = (a.N + BKV - 1) / BKV;
     hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kNWkv, bq_for<D>(), CAUSAL>), dim3(BH * nkb), dim3(kNWkv * 64), 0,
@@ -352,20 +352,21 @@ hipError_t go(const BwdArgs& a) {
                        (const uint16_t*)a.dO, delta, lse2, a.dk, a.dv, BH, a.N, c, a.scale);
     return hipGetLastError();
   }
+  return hipSuccess;
 }
 
 template <int D>
-hipError_t by_dtype(const BwdArgs& a) {
+hipError_t by_dtype(const BwdArgs& a, int stages) {
   switch (a.dtype) {
-    case kDtypeBF16: return a.causal ? go<bf16_t, D, true>(a) : go<bf16_t, D, false>(a);
-    case kDtypeF16: return a.causal ? go<f16_t, D, true>(a) : go<f16_t, D, false>(a);
+    case kDtypeBF16: return a.causal ? go<bf16_t, D, true>(a, stages) : go<bf16_t, D, false>(a, stages);
+    case kDtypeF16: return a.causal ? go<f16_t, D, true>(a, stages) : go<f16_t, D, false>(a, stages);
   }
   return hipErrorInvalidValue;
 }
 }  // namespace
 
-hipError_t launch_backward(const BwdArgs& a) {
-  return a.d == 64 ? by_dtype<64>(a) : by_dtype<128>(a);
+hipError_t launch_backward(const BwdArgs& a, int stages) {
+  return a.d == 64 ? by_dtype<64>(a, stages) : by_dtype<128>(a, stages);
 }
 
 }  // namespace fa

@@ -42,7 +42,10 @@ struct BwdArgs {
   hipStream_t stream;
 };
 
+constexpr int kStageDq = 1;    // dQ kernel (also writes D and lse*log2(e))
+constexpr int kStageDkdv = 2;  // dK/dV kernel (reads D and lse*log2(e))
+
 hipError_t launch_forward(const FwdArgs& a);
-hipError_t launch_backward(const BwdArgs& a);
+hipError_t launch_backward(const BwdArgs& a, int stages);
 
 }  // namespace fa

@@ -108,15 +108,38 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
  *                   16-byte aligned; its contents on entry are ignored.
  * The score tiles are recomputed from Q, K and lse ("FlashAttention：IO 感知…",
  * 方法细节; "Flash Attention", FlashAttention section on training): with
- * P = exp(scale*QK^T - lse), dV = P^T dO, dP = dO V^T, D_i = dO_i . O_i,
- * dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
- * The result is deterministic (no atomics).  Returns FA_OK or a negative fa_status_t.
+ * P = exp(scale*QK^T - lse), dV = P^T dO, dP = dO V^T, D_i = sum_j P_ij dP_ij
+ * (= dO_i . O_i), dS = P * (dP - D), dQ = scale dS K, dK = scale dS^T Q.
+ * D is summed from the recomputed fp32 P and dP rather than from the 16-bit o, and P
+ * and dS enter the products as hi + lo 16-bit pairs; o is checked (non-NULL, aligned)
+ * but its values are not read.  The result is deterministic (no atomics).
+ * Equivalent to fa_backward_dq followed by fa_backward_dkdv on the same stream and
+ * workspace.  Returns FA_OK or a negative fa_status_t.
  */
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO,
                 const float* lse, float* dq, float* dk, float* dv,
                 void* workspace, size_t workspace_bytes,
                 int B, int H, int N, int d, float scale, int causal,
                 fa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * fa_backward_dq -- first stage of fa_backward: dq, and D_i and lse_i*log2(e) into
+ * `workspace` for the second stage.  Arguments as for fa_backward.
+ */
+int fa_backward_dq(const void* q, const void* k, const void* v, const void* dO,
+                   const float* lse, float* dq, void* workspace, size_t workspace_bytes,
+                   int B, int H, int N, int d, float scale, int causal,
+                   fa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * fa_backward_dkdv -- second stage of fa_backward: dk and dv, reading the workspace a
+ * preceding fa_backward_dq with the same arguments filled (on the same stream, or
+ * ordered after it by the caller).  Arguments as for fa_backward.
+ */
+int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dO,
+                     float* dk, float* dv, const void* workspace, size_t workspace_bytes,
+                     int B, int H, int N, int d, float scale, int causal,
+                     fa_dtype_t dtype, hipStream_t stream);
 
 /* fa_status_string -- static, human-readable text for a status code. */
 const char* fa_status_string(int status);
