@@ -177,7 +177,10 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rs, int vo
   return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// s_waitcnt vmcnt(0) (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15).  A builtin, not inline
+// asm: inline asm makes the compiler assume AGPRs may be in use and select the AGPR form of
+// every MFMA, which then costs a copy for each accumulator the VALU touches.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Value of x held by lane l^32 (the other half of the wave): v_permlane32_swap.
 __device__ __forceinline__ float other_half(float x) {

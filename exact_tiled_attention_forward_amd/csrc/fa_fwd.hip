@@ -11,6 +11,7 @@
 // not computed (same page, FlashAttention-2 section).
 //
 // Mapping to CDNA4 (one wave = 64 lanes owns 32 query rows):
+//   * o and l are rescaled only when a row's max moved by more than 8 in log2 units.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16: K (A operand) is read row-wise from LDS, Q (B
 //     operand) stays in registers for the whole kernel.  In the accumulator, lane l holds
 //     query l%32 and 16 of the tile's 32 keys, so the row max and row sum are in-lane
@@ -31,14 +32,26 @@ namespace fa {
 // ----------------------------------------------------------------------------------
 // 16-bit inputs (bf16 or fp16), fp32 accumulation.
 //   NW waves per workgroup, 32 query rows per wave -> BR = 32*NW rows per workgroup.
-//   BC keys per tile.
+//   BC keys per tile; K and V tiles double-buffered in LDS, the next tile's fetch issued
+//   right after the barrier so it overlaps this tile's math.
+//
+// Lazy rescaling: the exponent reference m of a row only moves when a tile's max exceeds
+// it by more than kRescaleSlack (log2 units).  Until then p = exp2(s*c - m) <= 2^slack and
+// o, l need no rescale: exp2(s - m_old) exp2(m_old - m_new) = exp2(s - m_new) holds for
+// any reference, so O = o/l and lse = m + log2(l) are unchanged.  The decision is
+// wave-uniform (one branch per tile) and after the first tiles of a row it is almost
+// never taken, which removes the multiply of every accumulator by alpha from the loop.
+//
+// Two workgroups share a CU (LDS and registers fit two), so the two waves on each SIMD
+// come from different workgroups and drift out of phase: one wave's MFMAs run while the
+// other wave's softmax runs on the VALU.
 // ----------------------------------------------------------------------------------
+constexpr float kRescaleSlack = 8.0f;
+
 template <class T, int D, int NW, int BC, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void fwd16_kernel(const uint16_t* __restrict__ Q,
-                                                        const uint16_t* __restrict__ K,
-                                                        const uint16_t* __restrict__ V,
-                                                        uint16_t* __restrict__ O, float* __restrict__ LSE,
-                                                        int BH, int N, float c) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd16_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int N, float c) {
   constexpr int BR = 32 * NW;
   constexpr int NT = NW * 64;
   constexpr int TB = BC * D * 2;  // bytes of one K or V tile
@@ -74,8 +87,9 @@ __global__ __launch_bounds__(NW * 64) void fwd16_kernel(const uint16_t* __restri
 #pragma unroll
   for (int st = 0; st < DS; ++st) qf[st] = buffer_load16(rq, qrow * (D * 2) + ((2 * st + half) << 4));
 
-  // base-2 running max m (of s*c); this half's running sums: l of the fp32 probabilities
-  // (for the logsumexp) and lr of the same probabilities rounded to 16 bits (for O)
+  // base-2 exponent reference m (of s*c); this half's running sums: l of the fp32
+  // probabilities (for the logsumexp) and lr of the same probabilities rounded to 16 bits
+  // (for O)
   float m = -INFINITY, l = 0.f, lr = 0.f;
   f32x16 o[DB];
 #pragma unroll
@@ -110,37 +124,40 @@ __global__ __launch_bounds__(NW * 64) void fwd16_kernel(const uint16_t* __restri
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + 32 * kb + acc_row(i, half);
-          if (key >= N || (CAUSAL && key > qrow)) s[kb][i] = -INFINITY;
+          s[kb][i] = (key >= N || (CAUSAL && key > qrow)) ? -INFINITY : s[kb][i];
         }
     }
 
-    // online softmax: new running max, rescale factor, exponentials
+    // online softmax: row max, lazy rescale, exponentials, sums, 16-bit P
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = max_halves(mx);
-    const float m_new = fmaxf(m, mx * c);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
+      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
+    mx = max_halves(mx) * c;
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m, mx);  // finite: the first tile always holds key 0
+      const float alpha = fast_exp2(m - m_new);
+      l *= alpha;
+      lr *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      m = m_new;
+    }
     float rs = 0.f, rsr = 0.f;
     uint32_t pk[KB][8];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const float p0 = fast_exp2(fmaf(s[kb][2 * t], c, -m_use));
-        const float p1 = fast_exp2(fmaf(s[kb][2 * t + 1], c, -m_use));
+        const float p0 = fast_exp2(fmaf(s[kb][2 * t], c, -m));
+        const float p1 = fast_exp2(fmaf(s[kb][2 * t + 1], c, -m));
         rs += p0 + p1;
         pk[kb][t] = T::pack(p0, p1);
         rsr = T::sum2(pk[kb][t], rsr);
       }
-    l = l * alpha + rs;
-    lr = lr * alpha + rsr;
-    m = m_new;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    l += rs;
+    lr += rsr;
 
     // O^T += V^T P^T
 #pragma unroll
