@@ -35,7 +35,7 @@ namespace fa {
 // 1. dQ (and D, lse2).  NW waves x 32 queries per workgroup; BC keys per tile.
 // ----------------------------------------------------------------------------------
 template <class T, int D, int NW, int BC, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
                                                          const uint16_t* __restrict__ V,
                                                          const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
                                                          float* __restrict__ delta, float* __restrict__ lse2,
@@ -323,7 +323,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const uint16_t* __res
 // ----------------------------------------------------------------------------------
 namespace {
 constexpr int kNWkv = 4;
-constexpr int kNWq = 4, kBCq = 64;
+constexpr int kNWq = 4, kBCq = 32;
 
 template <int D>
 constexpr int bq_for() { return D == 128 ? 32 : 64; }
