@@ -202,6 +202,11 @@ __device__ __forceinline__ float sum_halves(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// max(a, b) with NaN propagation (IEEE 754-2019 maximum).  Chains of it lower to
+// v_maximum3_f32, one instruction per two new values; fmaxf would first canonicalise
+// every input (quieting signalling NaNs), which doubles the work of a row max.
+__device__ __forceinline__ float max_nan(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Row index (within a 32-row accumulator tile) held in register i by this lane's half.
 __device__ __forceinline__ constexpr int acc_row(int i, int half) {
   return 8 * (i >> 2) + 4 * half + (i & 3);

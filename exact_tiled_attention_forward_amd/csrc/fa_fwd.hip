@@ -42,14 +42,13 @@ namespace fa {
 // wave-uniform (one branch per tile) and after the first tiles of a row it is almost
 // never taken, which removes the multiply of every accumulator by alpha from the loop.
 //
-// Two workgroups share a CU (LDS and registers fit two), so the two waves on each SIMD
-// come from different workgroups and drift out of phase: one wave's MFMAs run while the
-// other wave's softmax runs on the VALU.
+// Several waves share each SIMD (two at d = 128, four at d = 64), so while one wave's
+// MFMAs run another wave's softmax runs on the VALU.
 // ----------------------------------------------------------------------------------
 constexpr float kRescaleSlack = 8.0f;
 
-template <class T, int D, int NW, int BC, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd16_kernel(
+template <class T, int D, int NW, int BC, int WPE, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void fwd16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int N, float c) {
   constexpr int BR = 32 * NW;
@@ -133,7 +132,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = fmaxf(mx, fmaxf(s[kb][i], s[kb][i + 1]));
+      for (int i = 0; i < 16; i += 2) mx = max_nan(max_nan(mx, s[kb][i]), s[kb][i + 1]);
     mx = max_halves(mx) * c;
     if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
       const float m_new = fmaxf(m, mx);  // finite: the first tile always holds key 0
@@ -325,15 +324,27 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
 // launchers
 // ----------------------------------------------------------------------------------
 namespace {
-constexpr int kNW16 = 4, kBC16 = 64;
+// Tile shapes per head dimension (waves per workgroup, keys per tile, waves per SIMD):
+//   d = 128: 8 waves x 32 rows = 256 query rows against 128-key tiles; K and V double
+//            buffered take 128 KiB of LDS, so one workgroup (two waves per SIMD) per CU.
+//            The larger query block halves the LDS fill traffic per score.
+//   d = 64:  8 waves against 64-key tiles at four waves per SIMD (128 VGPRs): the
+//            softmax dominates at this head size, and more resident waves hide it.
+template <int D>
+struct Fwd16Shape;
+template <>
+struct Fwd16Shape<128> { static constexpr int NW = 8, BC = 128, WPE = 2; };
+template <>
+struct Fwd16Shape<64> { static constexpr int NW = 8, BC = 64, WPE = 4; };
 constexpr int kNW32 = 2, kBC32 = 32;
 
 template <class T, int D, bool CAUSAL>
 hipError_t go16(const FwdArgs& a) {
-  constexpr int BR = 32 * kNW16;
+  using S = Fwd16Shape<D>;
+  constexpr int BR = 32 * S::NW;
   const int nqb = (a.N + BR - 1) / BR;
-  hipLaunchKernelGGL((fwd16_kernel<T, D, kNW16, kBC16, CAUSAL>), dim3(a.B * a.H * nqb), dim3(kNW16 * 64), 0, a.stream,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
+  hipLaunchKernelGGL((fwd16_kernel<T, D, S::NW, S::BC, S::WPE, CAUSAL>), dim3(a.B * a.H * nqb), dim3(S::NW * 64), 0,
+                     a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                      a.B * a.H, a.N, a.scale * kLog2e);
   return hipGetLastError();
 }
