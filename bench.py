@@ -71,6 +71,112 @@ def stored_traffic(kernel: str, workload: str):
         return None
 
 
+KERNEL_KEYS = (("fwd16_kernel", "fwd"), ("fwd32_kernel", "fwd"), ("bwd_dq_kernel", "bwd_dq"),
+               ("bwd_dkdv_kernel", "bwd_dkdv"))
+
+
+def kernel_key(name: str):
+    """Bench name of a library kernel from its demangled name (None for other kernels)."""
+    for frag, key in KERNEL_KEYS:
+        if f"fa::{frag}" in name:
+            return key
+    return None
+
+
+def algorithmic_bytes(w):
+    """HBM bytes each kernel must move at least: its inputs read once, its outputs written
+    once.  fwd reads Q, K, V and writes O and the logsumexp; bwd_dq reads Q, K, V, dO and
+    the logsumexp and writes fp32 dQ plus D and lse*log2(e); bwd_dkdv reads Q, K, V, dO, D
+    and lse*log2(e) and writes fp32 dK, dV."""
+    s = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
+    rows = w.B * w.H * w.N
+    return {"fwd": rows * (4 * w.d * s + 4), "bwd_dq": rows * (4 * w.d * s + 4 + 4 * w.d + 8),
+            "bwd_dkdv": rows * (4 * w.d * s + 8 + 8 * w.d)}
+
+
+def _read_counters(path):
+    """{kernel key or 'copy': {counter: [value per dispatch]}} from a rocprofv3 counter CSV."""
+    import csv
+    out = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            key = "copy" if "copyBuffer" in name else kernel_key(name)
+            if key is None:
+                continue
+            out.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def pmc_summary(fetch_csv, write_csv, w, copy_mb, command):
+    """Write profiles/traffic_<kernel>_<workload>.txt from two rocprofv3 --pmc runs (FETCH_SIZE,
+    then WRITE_SIZE; KiB per dispatch), each scaled by what the same counter reads for a
+    device-to-device copy of copy_mb MiB run in the same process."""
+    fetch, write = _read_counters(fetch_csv), _read_counters(write_csv)
+    mean = lambda v: sum(v) / len(v)
+    copy_bytes = copy_mb * 2.0 ** 20
+    f_scale = copy_bytes / (mean(fetch["copy"]["FETCH_SIZE"]) * 1024)
+    w_scale = copy_bytes / (mean(write["copy"]["WRITE_SIZE"]) * 1024)
+    alg = algorithmic_bytes(w)
+    digest = kernel_source_digest()
+    written = []
+    for key in ("fwd", "bwd_dq", "bwd_dkdv"):
+        if key not in fetch or key not in write:
+            continue
+        fk, wk = mean(fetch[key]["FETCH_SIZE"]), mean(write[key]["WRITE_SIZE"])
+        traffic = fk * 1024 * f_scale + wk * 1024 * w_scale
+        path = os.path.join(PROFILES, f"traffic_{key}_{w.name}.txt")
+        with open(path, "w") as f:
+            f.write(f"# HBM traffic of the {key} kernel on {w.name} (B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype}"
+                    f"{' causal' if w.causal else ''}), rocprofv3 derived counters per dispatch\n")
+            f.write(f"kernel: {key}\nworkload: {w.name}\nsource_sha256: {digest}\n")
+            f.write(f"dispatches: {len(fetch[key]['FETCH_SIZE'])}\n")
+            f.write(f"fetch_kib_per_dispatch: {fk:.1f}\nwrite_kib_per_dispatch: {wk:.1f}\n")
+            f.write(f"copy_calibration: device-to-device copy of {copy_mb} MiB reads "
+                    f"{mean(fetch['copy']['FETCH_SIZE']):.1f} KiB and writes {mean(write['copy']['WRITE_SIZE']):.1f} KiB "
+                    f"per dispatch (expected {copy_bytes / 1024:.1f})\n")
+            f.write(f"fetch_scale: {f_scale:.4f}\nwrite_scale: {w_scale:.4f}\n")
+            f.write(f"traffic_bytes_per_launch: {traffic:.0f}\n")
+            f.write(f"algorithmic_bytes_per_launch: {alg[key]}\n")
+            f.write(f"traffic_over_algorithmic: {traffic / alg[key]:.3f}\n")
+            f.write(f"command: {command}\n")
+        written.append(path)
+    return written
+
+
+def trace_summary(stats_csv, bench_log, w, command):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run of this script."""
+    import csv
+    rows = []
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            if kernel_key(r["Name"]) is None:
+                continue
+            name = r["Name"].split("(")[0].replace("void ", "")
+            rows.append((name, int(r["Calls"]), float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+                         float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    line = None
+    with open(bench_log) as f:
+        for ln in f:
+            if ln.startswith("{") and '"metric"' in ln:
+                line = json.loads(ln)
+    path = os.path.join(PROFILES, f"kernel_trace_{w.name}.md")
+    with open(path, "w") as f:
+        f.write(f"# Kernel trace: {w.name} (B={w.B}, H={w.H}, N={w.N}, d={w.d}, {w.dtype}"
+                f"{', causal' if w.causal else ''}), {'forward + backward' if w.backward else 'forward'}\n\n")
+        f.write(f"Command (from the repository root on one MI355X):\n\n```\n{command}\n```\n\n")
+        f.write("| kernel | calls | avg (us) | min (us) | max (us) | share of GPU time |\n|---|---|---|---|---|---|\n")
+        for r in rows:
+            f.write(f"| `{r[0]}` | {r[1]} | {r[2]:.1f} | {r[3]:.1f} | {r[4]:.1f} | {r[5]:.1f}% |\n")
+        if line:
+            f.write("\nHIP-event averages measured inside the same run (ms): "
+                    + ", ".join(f"{k} {v}" for k, v in line["kernel_ms"].items()) + "\n")
+            f.write(f"Bench line: value {line['value']} TFLOP/s ({line['pct_of_peak']}% of {PEAK_BF16_TFLOPS}), "
+                    f"forward {line['fwd_tflops']} TFLOP/s ({line['fwd_pct_of_peak']}%), roofline kernel "
+                    f"{line['roofline']['kernel']} at {line['roofline']['achieved']} TFLOP/s algorithmic.\n")
+    return path
+
+
 def kernel_flops(w):
     """Credited (algorithmic) flops of each kernel per launch.  The forward kernel owns
     S = QK^T and O = PV; of the backward's five products the dK/dV kernel owns S, dP,
@@ -118,7 +224,25 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large_head_causal")
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads of the CPU oracle sample (0: skip)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after timing, run device-to-device copies of MIB MiB (a known-traffic kernel for "
+                         "rocprofv3 --pmc calibration)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: write profiles/traffic_*.txt from two rocprofv3 --pmc runs")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("STATS_CSV", "BENCH_LOG"),
+                    help="no GPU: write profiles/kernel_trace_<workload>.md from a --kernel-trace --stats run")
+    ap.add_argument("--command", default="", help="command line recorded in the summaries")
     args = ap.parse_args()
+
+    if args.pmc_summary or args.trace_summary:
+        from exact_tiled_attention_forward_amd.workloads import WORKLOADS
+        w = WORKLOADS[args.workload]
+        if args.pmc_summary:
+            for p in pmc_summary(*args.pmc_summary, w, args.copy_calibration, args.command):
+                log("wrote", p)
+        if args.trace_summary:
+            log("wrote", trace_summary(*args.trace_summary, w, args.command))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -218,6 +342,13 @@ def main():
         line["bwd_pct_of_peak"] = round(100 * bwd_tf / PEAK_BF16_TFLOPS, 2)
     log(f"{w.name}: step {ms_per_step:.3f} ms, {value:.1f} TFLOP/s; kernels (ms): "
         + ", ".join(f"{n} {t:.3f}" for n, t in kernel_ms.items()))
+    if args.copy_calibration > 0:
+        src = torch.empty(args.copy_calibration << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.cpu_heads > 0:
         log(f"timing the fp64 CPU oracle on {args.cpu_heads} heads ...")
         line["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_heads)
