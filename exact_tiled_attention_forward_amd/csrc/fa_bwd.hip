@@ -22,10 +22,11 @@
 //             dP^T = V dO^T, D_i = sum_j P_ij dP_ij.  Pass 2: the same tiles again,
 //             dS^T = P^T (dP^T - D), dQ^T += K^T dS^T (K^T by ds_read_b64_tr_b16).
 //             Writes D and lse*log2(e) to the workspace for kernel 2.
-//   2. dkdv:  one workgroup per (batch, head, block of 32*NW keys), K and V in
-//             registers, Q and dO tiles (and their D, lse) streamed through LDS.
-//             S = Q K^T, dP = dO V^T (lane = key), then dV^T += dO^T P and
-//             dK^T += Q^T dS with dO^T / Q^T from transposing LDS reads.
+//   2. dkdv:  one workgroup per (batch, head, block of 32*NP keys), Q and dO tiles (and
+//             their D, lse) streamed through LDS.  Per 32 keys a pair of waves: one
+//             holds K, computes S = Q K^T, P and dV^T += dO^T P; the other holds V,
+//             computes dP = dO V^T, dS and dK^T += Q^T dS (dO^T / Q^T from transposing
+//             LDS reads), with P handed over through LDS.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -164,41 +165,52 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 }
 
 // ----------------------------------------------------------------------------------
-// 2. dK, dV.  NW waves x 32 keys per workgroup; BQ queries per streamed tile.
+// 2. dK, dV.  NP wave pairs per workgroup, 32 keys per pair; BQ queries per streamed tile.
+//
+// The two waves of a pair share their 32 keys and split the work by operand:
+//   wave A (rows 0..NP-1):  K in registers.  S = Q K^T, P = exp2(S c - lse2), P to LDS,
+//                           dV^T += dO^T (P hi + P lo).
+//   wave B (rows NP..2NP-1): V in registers.  dP = dO V^T, P from LDS,
+//                           dS = P (dP - D), dK^T += Q^T (dS hi + dS lo).
+// Each wave holds one operand block and one accumulator (about 170 VGPRs instead of the
+// 270 one wave doing all of it needs), so two waves fit per SIMD.  Waves w and w + NP
+// land on the same SIMD: while one runs its softmax arithmetic on the VALU the other's
+// products run on the matrix core.  Per tile: barrier (Q, dO, statistics in LDS), A
+// computes and publishes P while B computes dP, barrier, both finish their products.
 // ----------------------------------------------------------------------------------
-template <class T, int D, int NW, int BQ, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                                                           const uint16_t* __restrict__ V,
-                                                           const uint16_t* __restrict__ dO,
-                                                           const float* __restrict__ delta,
-                                                           const float* __restrict__ lse2, float* __restrict__ dK,
-                                                           float* __restrict__ dV, int BH, int N, float c,
-                                                           float scale) {
-  constexpr int BKV = 32 * NW;
+template <class T, int D, int NP, int BQ, bool CAUSAL>
+__global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ delta, const float* __restrict__ lse2,
+    float* __restrict__ dK, float* __restrict__ dV, int BH, int N, float c, float scale) {
+  constexpr int NW = 2 * NP;
+  constexpr int BKV = 32 * NP;
   constexpr int NT = NW * 64;
   constexpr int TB = BQ * D * 2;
   constexpr int QB = BQ / 32;  // 32-query accumulator blocks per tile
   constexpr int DS = D / 16;
   constexpr int DB = D / 32;
+  constexpr int PB = QB * 16 * 64 * 4;  // bytes of one pair's P tile (QB accumulators, 64 lanes)
   static_assert(BQ % 32 == 0 && BQ <= 64, "query tile");
-  // Q0 Q1 dO0 dO1, then [buffer][lse2 | delta][64 floats]: a dword DMA instruction
-  // writes all 64 lanes, so each array gets a full 64-float slot
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TB + 2 * 2 * 64 * 4];
+  // Q0 Q1 dO0 dO1 | stats [buffer][lse2 | delta][64 floats] (a dword DMA instruction writes
+  // all 64 lanes, so each array gets a full 64-float slot) | P exchange [pair]
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TB + 2 * 2 * 64 * 4 + NP * PB];
   FA_LDS uint8_t* lds = (FA_LDS uint8_t*)(smem);
   FA_LDS float* stats = (FA_LDS float*)(smem + 4 * TB);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, c32 = lane & 31;
+  const bool role_b = wave >= NP;
+  const int pair = role_b ? wave - NP : wave;
+  FA_LDS f32x4* pex = (FA_LDS f32x4*)(smem + 4 * TB + 2 * 2 * 64 * 4 + pair * PB);
   const int bh = blockIdx.x % BH;
   const int kblk = blockIdx.x / BH;  // causal: block 0 sees the most queries and starts first
   const int k0 = kblk * BKV;
-  const int kw0 = k0 + 32 * wave;
+  const int kw0 = k0 + 32 * pair;
   const int krow = kw0 + c32;
 
   const size_t head = (size_t)bh * N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const auto rq = make_rsrc(Q + head, head_bytes);
-  const auto rk = make_rsrc(K + head, head_bytes);
-  const auto rv = make_rsrc(V + head, head_bytes);
   const auto rdo = make_rsrc(dO + head, head_bytes);
   const auto rl = make_rsrc(lse2 + (size_t)bh * N, (uint32_t)N * 4);
   const auto rd = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4);
@@ -220,20 +232,17 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const uint16_t* __res
 
   if (qt0 < nqt) load_tile(qt0, 0);
 
-  // this wave's keys and values as B operands (lane = key, 8 consecutive d per lane)
-  u32x4 kf[DS], vf[DS];
+  // this wave's keys (A) or values (B) as B operands (lane = key, 8 consecutive d per lane)
+  u32x4 kv[DS];
+  {
+    const auto rkv = make_rsrc((role_b ? V : K) + head, head_bytes);
 #pragma unroll
-  for (int st = 0; st < DS; ++st) {
-    kf[st] = buffer_load16(rk, krow * (D * 2) + ((2 * st + half) << 4));
-    vf[st] = buffer_load16(rv, krow * (D * 2) + ((2 * st + half) << 4));
+    for (int st = 0; st < DS; ++st) kv[st] = buffer_load16(rkv, krow * (D * 2) + ((2 * st + half) << 4));
   }
 
-  f32x16 dk[DB], dv[DB];
+  f32x16 acc[DB];  // dV^T (A) or dK^T (B): lane = key, registers = head-dimension rows
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    dk[db] = (f32x16){};
-    dv[db] = (f32x16){};
-  }
+  for (int db = 0; db < DB; ++db) acc[db] = (f32x16){};
 
   for (int qt = qt0; qt < nqt; ++qt) {
     wait_vmem();
@@ -241,79 +250,93 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const uint16_t* __res
     const int cur = (qt - qt0) & 1;
     if (qt + 1 < nqt) load_tile(qt + 1, cur ^ 1);
     const int q0 = qt * BQ;
-    if (CAUSAL && q0 + BQ - 1 < kw0) continue;  // every query of the tile precedes this wave's keys
+    // every query of the tile precedes this pair's keys: P = 0 (both waves of the pair
+    // agree, and both still meet the barrier below)
+    const bool active = !(CAUSAL && q0 + BQ - 1 < kw0);
     const FA_LDS uint8_t* qtile = lds + cur * TB;
     const FA_LDS uint8_t* otile = lds + (2 + cur) * TB;
     const FA_LDS float* l2 = stats + cur * 128;
     const FA_LDS float* dl = l2 + 64;
     const bool need_mask = (q0 + BQ > N) || (CAUSAL && q0 < kw0 + 31);
 
-    uint32_t ph[QB][8], pl[QB][8], sh[QB][8], sl[QB][8];
+    // phase 1: A computes P and publishes it, B computes dP
+    f32x16 x[QB];  // A: P, B: dP (rows = queries q0 + 32*qb + acc_row(i, half))
+    if (active) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        x[qb] = (f32x16){};
+#pragma unroll
+        for (int st = 0; st < DS; ++st)
+          x[qb] = T::mfma(lds_row16<D>(role_b ? otile : qtile, 32 * qb + c32, 2 * st + half), kv[st], x[qb]);
+      }
+      if (!role_b) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const int r0 = 32 * qb + 8 * a + 4 * half;
+            const f32x4 lv = *(const FA_LDS f32x4*)(l2 + r0);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int i = 4 * a + e;
+              float p = fast_exp2(fmaf(x[qb][i], c, -lv[e]));
+              if (need_mask) {
+                const int q = q0 + r0 + e;
+                if (q >= N || (CAUSAL && krow > q)) p = 0.f;
+              }
+              x[qb][i] = p;
+            }
+            pex[(qb * 4 + a) * 64 + lane] = (f32x4){x[qb][4 * a], x[qb][4 * a + 1], x[qb][4 * a + 2], x[qb][4 * a + 3]};
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (!active) continue;
+
+    // phase 2: A: dV^T += dO^T (P hi + P lo);  B: dS = P (dP - D), dK^T += Q^T (dS hi + dS lo)
+    uint32_t hi[QB][8], lo[QB][8];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      f32x16 s = (f32x16){}, dp = (f32x16){};
+      if (role_b) {
 #pragma unroll
-      for (int st = 0; st < DS; ++st) {
-        s = T::mfma(lds_row16<D>(qtile, 32 * qb + c32, 2 * st + half), kf[st], s);
-        dp = T::mfma(lds_row16<D>(otile, 32 * qb + c32, 2 * st + half), vf[st], dp);
-      }
-      // rows of this accumulator: queries q0 + 32*qb + acc_row(i, half)
+        for (int a = 0; a < 4; ++a) {
+          const int r0 = 32 * qb + 8 * a + 4 * half;
+          const f32x4 dlv = *(const FA_LDS f32x4*)(dl + r0);
+          const f32x4 pv = pex[(qb * 4 + a) * 64 + lane];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int r0 = 32 * qb + 8 * a + 4 * half;
-        const f32x4 lv = *(const FA_LDS f32x4*)(l2 + r0);
-        const f32x4 dlv = *(const FA_LDS f32x4*)(dl + r0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * a + e;
-          float p = fast_exp2(fmaf(s[i], c, -lv[e]));
-          if (need_mask) {
-            const int q = q0 + r0 + e;
-            if (q >= N || (CAUSAL && krow > q)) p = 0.f;
-          }
-          s[i] = p;
-          dp[i] = p * (dp[i] - dlv[e]);
+          for (int e = 0; e < 4; ++e) x[qb][4 * a + e] = pv[e] * (x[qb][4 * a + e] - dlv[e]);
         }
       }
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        split2<T>(s[2 * t], s[2 * t + 1], ph[qb][t], pl[qb][t]);
-        split2<T>(dp[2 * t], dp[2 * t + 1], sh[qb][t], sl[qb][t]);
-      }
+      for (int t = 0; t < 8; ++t) split2<T>(x[qb][2 * t], x[qb][2 * t + 1], hi[qb][t], lo[qb][t]);
     }
-
-    // dV^T += dO^T (P hi + P lo),  dK^T += Q^T (dS hi + dS lo)
+    const FA_LDS uint8_t* atile = role_b ? qtile : otile;  // Q^T for dK, dO^T for dV
 #pragma unroll
     for (int ks = 0; ks < BQ / 16; ++ks) {
       const int qb = ks >> 1, mm = ks & 1;
-      const u32x4 bph = (u32x4){ph[qb][4 * mm], ph[qb][4 * mm + 1], ph[qb][4 * mm + 2], ph[qb][4 * mm + 3]};
-      const u32x4 bpl = (u32x4){pl[qb][4 * mm], pl[qb][4 * mm + 1], pl[qb][4 * mm + 2], pl[qb][4 * mm + 3]};
-      const u32x4 bsh = (u32x4){sh[qb][4 * mm], sh[qb][4 * mm + 1], sh[qb][4 * mm + 2], sh[qb][4 * mm + 3]};
-      const u32x4 bsl = (u32x4){sl[qb][4 * mm], sl[qb][4 * mm + 1], sl[qb][4 * mm + 2], sl[qb][4 * mm + 3]};
+      const u32x4 bh_ = (u32x4){hi[qb][4 * mm], hi[qb][4 * mm + 1], hi[qb][4 * mm + 2], hi[qb][4 * mm + 3]};
+      const u32x4 bl_ = (u32x4){lo[qb][4 * mm], lo[qb][4 * mm + 1], lo[qb][4 * mm + 2], lo[qb][4 * mm + 3]};
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const u32x4 ao = lds_colop<D>(otile, 16 * ks, 32 * db, lane);
-        dv[db] = T::mfma(ao, bph, dv[db]);
-        dv[db] = T::mfma(ao, bpl, dv[db]);
-        const u32x4 aq = lds_colop<D>(qtile, 16 * ks, 32 * db, lane);
-        dk[db] = T::mfma(aq, bsh, dk[db]);
-        dk[db] = T::mfma(aq, bsl, dk[db]);
+        const u32x4 a = lds_colop<D>(atile, 16 * ks, 32 * db, lane);
+        acc[db] = T::mfma(a, bh_, acc[db]);
+        acc[db] = T::mfma(a, bl_, acc[db]);
       }
     }
   }
 
   // lane = key (column of dK^T / dV^T), registers = head-dimension rows
   if (krow < N) {
-    float* dkr = dK + head + (size_t)krow * D;
-    float* dvr = dV + head + (size_t)krow * D;
+    float* out = (role_b ? dK : dV) + head + (size_t)krow * D;
+    const float f = role_b ? scale : 1.0f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * db + 8 * g + 4 * half;
-        *(f32x4*)(dkr + d) = (f32x4){dk[db][4 * g] * scale, dk[db][4 * g + 1] * scale, dk[db][4 * g + 2] * scale,
-                                     dk[db][4 * g + 3] * scale};
-        *(f32x4*)(dvr + d) = (f32x4){dv[db][4 * g], dv[db][4 * g + 1], dv[db][4 * g + 2], dv[db][4 * g + 3]};
+        *(f32x4*)(out + d) = (f32x4){acc[db][4 * g] * f, acc[db][4 * g + 1] * f, acc[db][4 * g + 2] * f,
+                                     acc[db][4 * g + 3] * f};
       }
   }
 }
@@ -322,7 +345,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_dkdv_kernel(const uint16_t* __res
 // launchers
 // ----------------------------------------------------------------------------------
 namespace {
-constexpr int kNWkv = 4;
+constexpr int kNPkv = 4;
 constexpr int kNWq = 4, kBCq = 32;
 
 template <int D>
@@ -345,9 +368,9 @@ hipError_t go(const BwdArgs& a, int stages) {
     if (e != hipSuccess) return e;
   }
   if (stages & kStageDkdv) {
-    constexpr int BKV = 32 * kNWkv;
+    constexpr int BKV = 32 * kNPkv;
     const int nkb = (a.N + BKV - 1) / BKV;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kNWkv, bq_for<D>(), CAUSAL>), dim3(BH * nkb), dim3(kNWkv * 64), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kNPkv, bq_for<D>(), CAUSAL>), dim3(BH * nkb), dim3(2 * kNPkv * 64), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dO, delta, lse2, a.dk, a.dv, BH, a.N, c, a.scale);
     return hipGetLastError();
