@@ -144,6 +144,39 @@ def pmc_summary(fetch_csv, write_csv, w, copy_mb, command):
     return written
 
 
+def counters_summary(csvs, w, command):
+    """profiles/counters_<kernel>_<workload>.txt: the mean per dispatch of every counter that
+    rocprofv3 --pmc collected for each library kernel (one CSV per counter pass)."""
+    vals = {}
+    for path in csvs:
+        for key, counters in _read_counters(path).items():
+            if key == "copy":
+                continue
+            for cname, v in counters.items():
+                vals.setdefault(key, {})[cname] = (sum(v) / len(v), len(v))
+    written = []
+    for key, counters in vals.items():
+        path = os.path.join(PROFILES, f"counters_{key}_{w.name}.txt")
+        with open(path, "w") as f:
+            f.write(f"# rocprofv3 counters of the {key} kernel on {w.name} (B={w.B} H={w.H} N={w.N} d={w.d} "
+                    f"{w.dtype}{' causal' if w.causal else ''}), mean per dispatch over all SEs/XCDs\n")
+            f.write(f"source_sha256: {kernel_source_digest()}\ncommand: {command}\n")
+            for cname in sorted(counters):
+                m, n = counters[cname]
+                f.write(f"{cname}: {m:.6g}   (dispatches: {n})\n")
+            c = {k: v[0] for k, v in counters.items()}
+            if "SQ_INSTS_MFMA" in c and "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                f.write(f"derived_mfma_busy_cycles_per_instruction: "
+                        f"{c['SQ_VALU_MFMA_BUSY_CYCLES'] / c['SQ_INSTS_MFMA']:.2f}\n")
+            if "SQ_INSTS_VALU" in c and "SQ_INSTS_MFMA" in c:
+                f.write(f"derived_valu_instructions_per_mfma: {(c['SQ_INSTS_VALU'] - c['SQ_INSTS_MFMA']) / c['SQ_INSTS_MFMA']:.2f}\n")
+            if "SQ_LDS_BANK_CONFLICT" in c and "SQ_INSTS_LDS" in c:
+                f.write(f"derived_lds_bank_conflict_cycles_per_lds_instruction: "
+                        f"{c['SQ_LDS_BANK_CONFLICT'] / max(c['SQ_INSTS_LDS'], 1):.4f}\n")
+        written.append(path)
+    return written
+
+
 def trace_summary(stats_csv, bench_log, w, command):
     """Markdown summary of a rocprofv3 --kernel-trace --stats run of this script."""
     import csv
@@ -175,6 +208,94 @@ def trace_summary(stats_csv, bench_log, w, command):
                     f"forward {line['fwd_tflops']} TFLOP/s ({line['fwd_pct_of_peak']}%), roofline kernel "
                     f"{line['roofline']['kernel']} at {line['roofline']['achieved']} TFLOP/s algorithmic.\n")
     return path
+
+
+def read_sclk():
+    """Current shader clock level from sysfs (e.g. '2400Mhz'), or None where unreadable."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                for ln in f:
+                    if ln.rstrip().endswith("*"):
+                        return ln.split(":", 1)[1].strip(" *\n")
+        except OSError:
+            continue
+    return None
+
+
+def sweep(names, reps: int, out_path: str):
+    """Time fa_forward (and the backward stages) of each workload with HIP events on the
+    stream they run on: median and min over `reps` back-to-back launches ("warm": inputs
+    may sit in the 256 MB last-level cache) and, for workloads whose inputs fit in that
+    cache, again with a 512 MB fill between launches ("cold")."""
+    import torch
+    import exact_tiled_attention_forward_amd as fa
+    from exact_tiled_attention_forward_amd.workloads import WORKLOADS, workload_inputs, elem_bytes
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    rows = []
+    for name in names:
+        w = WORKLOADS[name]
+        inp = workload_inputs(w)
+        q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        passes = {"fwd": lambda: fa.fa_forward(q, k, v, o, lse, causal=w.causal, stream=stream)}
+        if w.backward:
+            do = inp["do"].to(dev)
+            f32 = torch.float32
+            dq, dk, dv = (torch.empty(q.shape, dtype=f32, device=dev) for _ in range(3))
+            ws = torch.empty(fa.fa_backward_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
+            passes["fwd"]()
+            passes["bwd"] = lambda: fa.fa_backward(q, k, v, o, do, lse, dq, dk, dv, causal=w.causal, workspace=ws,
+                                                 stream=stream)
+        s = elem_bytes(w.dtype)
+        unit = 2.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
+        info = {"fwd": (2 * unit, w.B * w.H * w.N * (4 * w.d * s + 4)),
+                "bwd": (5 * unit, w.B * w.H * w.N * (5 * w.d * s + 3 * w.d * 4 + 8))}
+        small = 4 * w.B * w.H * w.N * w.d * s < (128 << 20)
+        for pname, fn in passes.items():
+            for mode in (["warm", "cold"] if small else ["warm"]):
+                for _ in range(10):
+                    fn()
+                ts = []
+                for _ in range(reps):
+                    if mode == "cold":
+                        flush.fill_(1)
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    fn()
+                    b.record(stream)
+                    b.synchronize()
+                    ts.append(a.elapsed_time(b))
+                ts.sort()
+                med, mn = ts[len(ts) // 2], ts[0]
+                flops, nbytes = info[pname]
+                rows.append({"workload": name, "shape": f"{w.B}x{w.H}x{w.N}x{w.d}", "dtype": w.dtype,
+                             "causal": w.causal, "pass": pname, "mode": mode, "median_us": med * 1e3,
+                             "min_us": mn * 1e3, "tflops": flops / (med * 1e-3) / 1e12,
+                             "pct_peak": 100 * flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                             "gbs": nbytes / (med * 1e-3) / 1e9})
+                log(f"{name} {pname} {mode}: {med * 1e3:.1f} us")
+        del q, k, v, o, lse, inp
+    sclk = read_sclk()
+    with open(out_path, "w") as f:
+        f.write("# Timing of every workload on one MI355X (HIP events on the launch stream)\n\n")
+        f.write(f"Command: `python3 bench.py --sweep --sweep-reps {reps}`; shader clock level read after the run: "
+                f"{sclk or 'not readable'}.\n")
+        f.write("TFLOP/s use 4BHN^2d (forward) and 10BHN^2d (backward), halved when causal; % of the 2516.6 "
+                "TFLOP/s bf16/fp16 dense MFMA peak (fp32 rows: the same figure, for comparison only); GB/s are "
+                "algorithmic bytes (inputs read once, outputs written once) over the median time.  cold = a "
+                "512 MB fill between launches.\n\n")
+        f.write("| workload | B x H x N x d | dtype | causal | pass | mode | median (us) | min (us) | TFLOP/s "
+                "| % peak | GB/s |\n|---|---|---|---|---|---|---|---|---|---|---|\n")
+        for r in rows:
+            f.write(f"| {r['workload']} | {r['shape']} | {r['dtype']} | {'yes' if r['causal'] else 'no'} | {r['pass']} "
+                    f"| {r['mode']} | {r['median_us']:.1f} | {r['min_us']:.1f} | {r['tflops']:.1f} | "
+                    f"{r['pct_peak']:.1f} | {r['gbs']:.0f} |\n")
+    return out_path
 
 
 def kernel_flops(w):
@@ -231,10 +352,15 @@ def main():
                     help="no GPU: write profiles/traffic_*.txt from two rocprofv3 --pmc runs")
     ap.add_argument("--trace-summary", nargs=2, metavar=("STATS_CSV", "BENCH_LOG"),
                     help="no GPU: write profiles/kernel_trace_<workload>.md from a --kernel-trace --stats run")
+    ap.add_argument("--counters-summary", nargs="+", metavar="CSV",
+                    help="no GPU: write profiles/counters_*.txt from rocprofv3 --pmc runs")
     ap.add_argument("--command", default="", help="command line recorded in the summaries")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time every workload (forward, backward) and write profiles/timing_all_workloads.md")
+    ap.add_argument("--sweep-reps", type=int, default=50)
     args = ap.parse_args()
 
-    if args.pmc_summary or args.trace_summary:
+    if args.pmc_summary or args.trace_summary or args.counters_summary:
         from exact_tiled_attention_forward_amd.workloads import WORKLOADS
         w = WORKLOADS[args.workload]
         if args.pmc_summary:
@@ -242,6 +368,9 @@ def main():
                 log("wrote", p)
         if args.trace_summary:
             log("wrote", trace_summary(*args.trace_summary, w, args.command))
+        if args.counters_summary:
+            for p in counters_summary(args.counters_summary, w, args.command):
+                log("wrote", p)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -249,6 +378,11 @@ def main():
         log("bench.py measures one GPU only: attention shards over (batch, head) with no exchange, "
             "and this library has no multi-GPU path.  Run with --gpus 1.")
         sys.exit(2)
+
+    if args.sweep:
+        names = ["single_head_f32", "prefill_bf16", "gpt2_medium_train", "long_f16", "long_bf16", "large_head_causal"]
+        log("wrote", sweep(names, args.sweep_reps, os.path.join(PROFILES, "timing_all_workloads.md")))
+        return
 
     import torch
     import exact_tiled_attention_forward_amd as fa

@@ -348,8 +348,8 @@ namespace {
 constexpr int kNPkv = 4;
 constexpr int kNWq = 4, kBCq = 32;
 
-template <int D>
-constexpr int bq_for() { return D == 128 ? 32 : 64; }
+// 64 queries per streamed Q/dO tile: two accumulator blocks per wave between barriers
+constexpr int kBQkv = 64;
 
 template <class T, int D, bool CAUSAL>
 hipError_t go(const BwdArgs& a, int stages) {
@@ -370,7 +370,7 @@ hipError_t go(const BwdArgs& a, int stages) {
   if (stages & kStageDkdv) {
     constexpr int BKV = 32 * kNPkv;
     const int nkb = (a.N + BKV - 1) / BKV;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kNPkv, bq_for<D>(), CAUSAL>), dim3(BH * nkb), dim3(2 * kNPkv * 64), 0,
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kNPkv, kBQkv, CAUSAL>), dim3(BH * nkb), dim3(2 * kNPkv * 64), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dO, delta, lse2, a.dk, a.dv, BH, a.N, c, a.scale);
     return hipGetLastError();

@@ -155,17 +155,23 @@ __device__ __forceinline__ void tile_load_async(FA_LDS uint8_t* tile, __amdgpu_b
   constexpr int CHUNKS = ROWS * CPR;
   constexpr int PER_INSTR = 64;
   constexpr int WAVES = NT / 64;
-  static_assert(CHUNKS % (PER_INSTR * WAVES) == 0, "tile must split evenly over waves");
+  constexpr int NI = CHUNKS / PER_INSTR;     // wave instructions per tile
+  static_assert(CHUNKS % PER_INSTR == 0 && (NI % WAVES == 0 || WAVES % NI == 0),
+                "tile must split evenly over waves");
   const int wave = tid >> 6, lane = tid & 63;
-#pragma unroll
-  for (int t = 0; t < CHUNKS / (PER_INSTR * WAVES); ++t) {
-    const int base = (t * WAVES + wave) * PER_INSTR;   // wave-uniform chunk index
+  auto issue = [&](int base) {  // base: wave-uniform chunk index
     const int p = base + lane;
     const int r = p / CPR;
     const int slot = p % CPR;
     const int c = slot ^ swz<D>(r);
     const int voff = (row0 + r) * (D * 2) + (c << 4);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)(tile + base * 16), 16, voff, 0, 0, 0);
+  };
+  if constexpr (NI % WAVES == 0) {
+#pragma unroll
+    for (int t = 0; t < NI / WAVES; ++t) issue((t * WAVES + wave) * PER_INSTR);
+  } else {
+    if (wave < NI) issue(wave * PER_INSTR);  // fewer instructions than waves: the first NI waves
   }
 }
 
