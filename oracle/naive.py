@@ -14,6 +14,16 @@ Readings where the pages are silent (each also listed in the design doc):
 * causal: key j is visible to query i iff j <= i (lower triangle, diagonal
   included; [FA-17] section 四 and the mask remark in section 五, [FA-ch]
   FlashAttention-2 section on fully masked blocks).  Masked scores are -inf.
+* query and key lengths may differ ([FA-blog] section 3.4: Q from the decoder,
+  K/V from the encoder or a growing cache).  With causal masking the N_q queries
+  are the last N_q positions of the N_k-long sequence (a decode step's query is the
+  newest token and sees the whole cache, [FA-17] section 五 on decode): key j is
+  visible to query i iff j <= i + (N_k - N_q).  N_q > N_k with causal masking
+  would leave rows with no visible key and is rejected.
+* grouped heads ([FA-17] section 四 names GQA as a mask-like variant orthogonal to
+  the tiling): H_q query heads share H_kv key/value heads, H_q = G * H_kv; query
+  head h reads key/value head h // G (consecutive query heads form a group).  In
+  the backward, the gradient of a shared K or V head is the sum over its group.
 * LSE_i = m_i + ln(l_i): the natural-log logsumexp of the scaled, masked row; the
   pages save (m, l) per row ([FA-ch] FlashAttention section on recomputation,
   [FA-nips] 方法细节), and m + ln l carries the same information.
@@ -32,6 +42,7 @@ import numpy as np
 
 __all__ = [
     "causal_mask",
+    "kv_head",
     "scores",
     "softmax_rows",
     "probabilities",
@@ -43,16 +54,31 @@ __all__ = [
 
 
 def causal_mask(n_q: int, n_k: int) -> np.ndarray:
-    """Boolean (n_q, n_k) array, True where key j is hidden from query i (j > i)."""
+    """Boolean (n_q, n_k) array, True where key j is hidden from query i.
+
+    The queries are the last n_q positions of an n_k-long sequence, so query i sits at
+    position i + (n_k - n_q) and sees keys j <= i + (n_k - n_q); for n_q == n_k this is
+    the plain lower triangle j <= i.
+    """
+    if n_q > n_k:
+        raise ValueError("causal attention needs n_q <= n_k (otherwise some query sees no key)")
     i = np.arange(n_q)[:, None]
     j = np.arange(n_k)[None, :]
-    return j > i
+    return j > i + (n_k - n_q)
+
+
+def kv_head(h: int, h_q: int, h_kv: int) -> int:
+    """Key/value head read by query head h: consecutive groups of h_q // h_kv query heads
+    share one key/value head."""
+    if h_q % h_kv:
+        raise ValueError("the query head count must be a multiple of the key/value head count")
+    return h // (h_q // h_kv)
 
 
 def scores(q: np.ndarray, k: np.ndarray, scale: float, causal: bool) -> np.ndarray:
     """S = scale * Q K^T for one head, masked scores set to -inf.
 
-    q: (N, d), k: (N, d) -> (N, N) float64.
+    q: (N_q, d), k: (N_k, d) -> (N_q, N_k) float64.
     """
     s = scale * (np.asarray(q, np.float64) @ np.asarray(k, np.float64).T)
     if causal:
@@ -90,19 +116,22 @@ def forward_head(q, k, v, scale: float, causal: bool):
 
 
 def forward(q, k, v, scale: float, causal: bool, heads=None):
-    """Attention forward over (B, H, N, d) inputs.
+    """Attention forward: q (B, H_q, N_q, d), k and v (B, H_kv, N_k, d).
 
-    Returns (O, LSE) as float64 arrays of shapes (B, H, N, d) and (B, H, N).  With
-    ``heads`` (an iterable of (b, h) pairs) only those heads are computed and the
-    other entries are NaN -- used to check sampled heads at full problem sizes.
+    Returns (O, LSE) as float64 arrays of shapes (B, H_q, N_q, d) and (B, H_q, N_q).
+    With ``heads`` (an iterable of (b, h) query-head pairs) only those heads are
+    computed and the other entries are NaN -- used to check sampled heads at full
+    problem sizes.
     """
-    q = np.asarray(q)
+    q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
     B, H, N, d = q.shape
+    Hkv = k.shape[1]
     o = np.full((B, H, N, v.shape[-1]), np.nan)
     lse = np.full((B, H, N), np.nan)
     todo = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
     for b, h in todo:
-        o[b, h], lse[b, h] = forward_head(q[b, h], k[b, h], v[b, h], scale, causal)
+        g = kv_head(h, H, Hkv)
+        o[b, h], lse[b, h] = forward_head(q[b, h], k[b, g], v[b, g], scale, causal)
     return o, lse
 
 
@@ -123,16 +152,28 @@ def backward_head(q, k, v, do, scale: float, causal: bool):
 
 
 def backward(q, k, v, do, scale: float, causal: bool, heads=None):
-    """Attention backward over (B, H, N, d) inputs -> (dQ, dK, dV) float64.
+    """Attention backward: q, dO (B, H_q, N_q, d), k, v (B, H_kv, N_k, d) ->
+    (dQ, dK, dV) float64 in the shapes of q, k and v.
 
-    ``heads`` restricts the computation to the listed (b, h) pairs (others NaN).
+    The gradient of a key/value head shared by a group of query heads is the sum of
+    the group's per-head gradients.  ``heads`` restricts the computation to the listed
+    (b, h_kv) key/value heads and every query head of their groups (others NaN); with
+    one query head per key/value head these are the (b, h) heads themselves.
     """
-    q = np.asarray(q)
+    q, k, v, do = np.asarray(q), np.asarray(k), np.asarray(v), np.asarray(do)
     B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    G = H // Hkv
+    kv_head(0, H, Hkv)  # validates the grouping
     dq = np.full(q.shape, np.nan)
-    dk = np.full(q.shape, np.nan)
-    dv = np.full(np.asarray(v).shape, np.nan)
-    todo = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
-    for b, h in todo:
-        dq[b, h], dk[b, h], dv[b, h] = backward_head(q[b, h], k[b, h], v[b, h], do[b, h], scale, causal)
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(v.shape, np.nan)
+    todo = [(b, g) for b in range(B) for g in range(Hkv)] if heads is None else list(heads)
+    for b, g in todo:
+        dk[b, g] = 0.0
+        dv[b, g] = 0.0
+        for h in range(g * G, (g + 1) * G):
+            dq[b, h], dkh, dvh = backward_head(q[b, h], k[b, g], v[b, g], do[b, h], scale, causal)
+            dk[b, g] += dkh
+            dv[b, g] += dvh
     return dq, dk, dv

@@ -225,6 +225,130 @@ def pin_backward_scaling(bwd, causal, n=9, d=4, seed=20):
         np.testing.assert_allclose(x, y, rtol=0, atol=1e-12)
 
 
+# ------------------------------------------------ query/key lengths that differ, grouped heads
+
+
+def pin_cross_sdpa(fwd, nq=7, nk=19, d=8, seed=21):
+    """N_q != N_k without a mask: torch SDPA (fp64, CPU) as the library routine."""
+    r = _rng(seed)
+    q = r.standard_normal((nq, d))
+    k, v = (r.standard_normal((nk, d)) for _ in range(2))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = fwd(q, k, v, scale, False)
+    tq, tk, tv = (torch.from_numpy(a)[None, None] for a in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale)[0, 0]
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+    s = torch.from_numpy(q) @ torch.from_numpy(k).T * scale
+    np.testing.assert_allclose(lse, torch.logsumexp(s, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+def pin_causal_suffix(fwd, n=23, nq=5, d=6, seed=22):
+    """Causal with N_q < N_k: the queries are the last N_q positions, so the result is
+    the last N_q rows of causal self-attention over the whole sequence (whose square
+    case the SDPA pin fixes).  Any other alignment of the mask fails this."""
+    r = _rng(seed)
+    q, k, v = (r.standard_normal((n, d)) for _ in range(3))
+    o_full, lse_full = fwd(q, k, v, 0.4, True)
+    for m in (nq, 1, n - 1):
+        o, lse = fwd(q[n - m:], k, v, 0.4, True)
+        np.testing.assert_allclose(o, o_full[n - m:], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(lse, lse_full[n - m:], rtol=0, atol=1e-13)
+
+
+def pin_decode_row(fwd, nk=17, d=5, seed=23):
+    """One causal query against N_k keys (a decode step) sees every key: it equals the
+    unmasked result."""
+    r = _rng(seed)
+    q = r.standard_normal((1, d))
+    k, v = (r.standard_normal((nk, d)) for _ in range(2))
+    o_c, lse_c = fwd(q, k, v, 0.9, True)
+    o_f, lse_f = fwd(q, k, v, 0.9, False)
+    np.testing.assert_array_equal(o_c, o_f)
+    np.testing.assert_array_equal(lse_c, lse_f)
+
+
+def pin_cross_autograd(bwd, nq=6, nk=15, d=4, seed=24):
+    """N_q != N_k gradients against torch autograd through fp64 SDPA (no mask)."""
+    r = _rng(seed)
+    q, do = (r.standard_normal((nq, d)) for _ in range(2))
+    k, v = (r.standard_normal((nk, d)) for _ in range(2))
+    scale = 0.7
+    tq, tk, tv = (torch.from_numpy(a)[None, None].requires_grad_(True) for a in (q, k, v))
+    torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=scale).backward(torch.from_numpy(do)[None, None])
+    dq, dk, dv = bwd(q, k, v, do, scale, False)
+    for x, t in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(x, t.grad[0, 0].numpy(), rtol=0, atol=1e-10)
+
+
+def pin_backward_suffix(bwd, n=14, nq=4, d=3, seed=25):
+    """Causal N_q < N_k gradients equal those of causal self-attention over the whole
+    sequence when only the last N_q rows of O carry a gradient (dO = 0 elsewhere)."""
+    r = _rng(seed)
+    q, k, v = (r.standard_normal((n, d)) for _ in range(3))
+    do = r.standard_normal((nq, d))
+    do_full = np.zeros((n, d))
+    do_full[n - nq:] = do
+    dq_f, dk_f, dv_f = bwd(q, k, v, do_full, 0.5, True)
+    dq, dk, dv = bwd(q[n - nq:], k, v, do, 0.5, True)
+    np.testing.assert_allclose(dq, dq_f[n - nq:], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk, dk_f, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, dv_f, rtol=0, atol=1e-12)
+
+
+def _gqa_inputs(seed, B=2, hkv=2, g=3, nq=9, nk=11, d=4):
+    r = _rng(seed)
+    q = r.standard_normal((B, hkv * g, nq, d))
+    k, v = (r.standard_normal((B, hkv, nk, d)) for _ in range(2))
+    do = r.standard_normal((B, hkv * g, nq, d))
+    return q, k, v, do
+
+
+def pin_gqa_sdpa(fwd_mh, causal, seed=26):
+    """Grouped heads (H_q = 3 H_kv) against torch SDPA with enable_gqa (fp64, CPU), and
+    against the one-head-per-group computation with K, V repeated per query head."""
+    q, k, v, _ = _gqa_inputs(seed)
+    g = q.shape[1] // k.shape[1]
+    o, lse = fwd_mh(q, k, v, 0.6, causal)
+    tq, tk, tv = (torch.from_numpy(a) for a in (q, k, v))
+    if causal:  # top-left and bottom-right coincide only when N_q == N_k
+        tk, tv = tk[:, :, :q.shape[2]], tv[:, :, :q.shape[2]]
+        o, lse = fwd_mh(q, k[:, :, :q.shape[2]], v[:, :, :q.shape[2]], 0.6, causal)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=0.6, enable_gqa=True)
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+    o_r, lse_r = fwd_mh(q, np.repeat(tk.numpy(), g, axis=1), np.repeat(tv.numpy(), g, axis=1), 0.6, causal)
+    np.testing.assert_array_equal(o, o_r)
+    np.testing.assert_array_equal(lse, lse_r)
+
+
+def pin_gqa_autograd(bwd_mh, causal, seed=27):
+    """Grouped-head gradients against torch autograd through fp64 SDPA with enable_gqa:
+    dK and dV of a shared head are the sums over its group."""
+    q, k, v, do = _gqa_inputs(seed, nk=9)
+    tq, tk, tv = (torch.from_numpy(a).requires_grad_(True) for a in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=0.6, enable_gqa=True)
+    out.backward(torch.from_numpy(do))
+    dq, dk, dv = bwd_mh(q, k, v, do, 0.6, causal)
+    for x, t in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(x, t.grad.numpy(), rtol=0, atol=1e-10)
+
+
+CROSS_FORWARD_PINS = [
+    ("cross_sdpa", pin_cross_sdpa),
+    ("causal_suffix", pin_causal_suffix),
+    ("decode_row", pin_decode_row),
+]
+
+CROSS_BACKWARD_PINS = [
+    ("cross_autograd", pin_cross_autograd),
+    ("backward_suffix", pin_backward_suffix),
+]
+
+GQA_FORWARD_PINS = [(f"gqa_sdpa_{'causal' if c else 'full'}", (lambda c: (lambda f: pin_gqa_sdpa(f, c)))(c))
+                    for c in (False, True)]
+GQA_BACKWARD_PINS = [(f"gqa_autograd_{'causal' if c else 'full'}", (lambda c: (lambda b: pin_gqa_autograd(b, c)))(c))
+                     for c in (False, True)]
+
+
 FORWARD_PINS = [
     ("worked_softmax", lambda f: pin_worked_softmax(f)),
     ("worked_two_block", lambda f: pin_worked_two_block(f)),

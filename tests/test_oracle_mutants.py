@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 
 from oracle import naive, tiled_ref
-from oracle_pins import BACKWARD_PINS, FORWARD_PINS
+from oracle_pins import (BACKWARD_PINS, CROSS_BACKWARD_PINS, CROSS_FORWARD_PINS, FORWARD_PINS, GQA_BACKWARD_PINS,
+                         GQA_FORWARD_PINS)
 
 
 def _fwd(mut):
@@ -20,6 +21,8 @@ def _fwd(mut):
             s = q @ k.T
         if causal:
             hidden = naive.causal_mask(*s.shape)
+            if mut == "top_left":  # ignores the offset of the query positions when N_q < N_k
+                hidden = np.arange(s.shape[1])[None, :] > np.arange(s.shape[0])[:, None]
             if mut == "mask_off_by_one":
                 hidden = np.arange(s.shape[1])[None, :] > np.arange(s.shape[0])[:, None] + 1
             s = np.where(hidden, -np.inf, s)
@@ -47,7 +50,12 @@ def _fwd(mut):
 def _bwd(mut):
     def bwd(q, k, v, do, scale, causal):
         q, k, v, do = (np.asarray(a, np.float64) for a in (q, k, v, do))
-        p = naive.probabilities(q, k, scale, causal)
+        if mut == "top_left" and causal:
+            s = scale * (q @ k.T)
+            s = np.where(np.arange(s.shape[1])[None, :] > np.arange(s.shape[0])[:, None], -np.inf, s)
+            p = naive.softmax_rows(s)[0]
+        else:
+            p = naive.probabilities(q, k, scale, causal)
         dv = (p @ do) if mut == "dv_untransposed" else (p.T @ do)
         dp = do @ v.T
         dsum = np.sum(p * dp, axis=-1, keepdims=True)
@@ -98,6 +106,68 @@ def test_backward_mutant_is_caught(mut):
         except (AssertionError, FloatingPointError, ValueError):
             failed.append(name)
     assert failed, f"mutant {mut} passed every backward pin"
+
+
+def _caught(pins, call):
+    failed = []
+    for name, pin in pins:
+        try:
+            call(pin)
+        except (AssertionError, FloatingPointError, ValueError):
+            failed.append(name)
+    return failed
+
+
+def test_cross_top_left_mask_is_caught():
+    """A causal mask aligned at the first key instead of the last query fails the
+    suffix pins (forward and backward); the unmutated copies pass them."""
+    assert not _caught(CROSS_FORWARD_PINS, lambda pin: pin(_fwd(None)))
+    assert not _caught(CROSS_BACKWARD_PINS, lambda pin: pin(_bwd(None)))
+    assert _caught(CROSS_FORWARD_PINS, lambda pin: pin(_fwd("top_left")))
+    assert _caught(CROSS_BACKWARD_PINS, lambda pin: pin(_bwd("top_left")))
+
+
+def _fwd_mh(mut):
+    def fwd(q, k, v, scale, causal):
+        B, H, nq, _ = q.shape
+        hkv = k.shape[1]
+        o = np.zeros(q.shape[:3] + (v.shape[-1],))
+        lse = np.zeros(q.shape[:3])
+        for b in range(B):
+            for h in range(H):
+                g = h % hkv if mut == "head_mod" else h // (H // hkv)
+                o[b, h], lse[b, h] = naive.forward_head(q[b, h], k[b, g], v[b, g], scale, causal)
+        return o, lse
+    return fwd
+
+
+def _bwd_mh(mut):
+    def bwd(q, k, v, do, scale, causal):
+        B, H = q.shape[:2]
+        hkv = k.shape[1]
+        dq = np.zeros(q.shape)
+        dk = np.zeros(k.shape)
+        dv = np.zeros(v.shape)
+        for b in range(B):
+            for h in range(H):
+                g = h // (H // hkv)
+                dq[b, h], dkh, dvh = naive.backward_head(q[b, h], k[b, g], v[b, g], do[b, h], scale, causal)
+                if mut == "no_group_sum":
+                    dk[b, g], dv[b, g] = dkh, dvh
+                else:
+                    dk[b, g] += dkh
+                    dv[b, g] += dvh
+        return dq, dk, dv
+    return bwd
+
+
+def test_gqa_mutants_are_caught():
+    """Query head h reading key/value head h % H_kv instead of h // G, and a shared
+    head's gradient taken from one query head instead of the group's sum, each fail."""
+    assert not _caught(GQA_FORWARD_PINS, lambda pin: pin(_fwd_mh(None)))
+    assert not _caught(GQA_BACKWARD_PINS, lambda pin: pin(_bwd_mh(None)))
+    assert _caught(GQA_FORWARD_PINS, lambda pin: pin(_fwd_mh("head_mod")))
+    assert _caught(GQA_BACKWARD_PINS, lambda pin: pin(_bwd_mh("no_group_sum")))
 
 
 def test_tiled_wrong_rescale_is_caught():

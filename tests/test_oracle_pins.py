@@ -6,7 +6,8 @@ import numpy as np
 import pytest
 
 from oracle import naive, tiled_ref
-from oracle_pins import BACKWARD_PINS, FORWARD_PINS, golden
+from oracle_pins import (BACKWARD_PINS, CROSS_BACKWARD_PINS, CROSS_FORWARD_PINS, FORWARD_PINS, GQA_BACKWARD_PINS,
+                         GQA_FORWARD_PINS, golden)
 
 
 @pytest.mark.parametrize("name,pin", FORWARD_PINS, ids=[n for n, _ in FORWARD_PINS])
@@ -17,6 +18,31 @@ def test_forward_pin(name, pin):
 @pytest.mark.parametrize("name,pin", BACKWARD_PINS, ids=[n for n, _ in BACKWARD_PINS])
 def test_backward_pin(name, pin):
     pin(naive.forward_head, naive.backward_head)
+
+
+@pytest.mark.parametrize("name,pin", CROSS_FORWARD_PINS, ids=[n for n, _ in CROSS_FORWARD_PINS])
+def test_cross_forward_pin(name, pin):
+    pin(naive.forward_head)
+
+
+@pytest.mark.parametrize("name,pin", CROSS_BACKWARD_PINS, ids=[n for n, _ in CROSS_BACKWARD_PINS])
+def test_cross_backward_pin(name, pin):
+    pin(naive.backward_head)
+
+
+@pytest.mark.parametrize("name,pin", GQA_FORWARD_PINS, ids=[n for n, _ in GQA_FORWARD_PINS])
+def test_gqa_forward_pin(name, pin):
+    pin(naive.forward)
+
+
+@pytest.mark.parametrize("name,pin", GQA_BACKWARD_PINS, ids=[n for n, _ in GQA_BACKWARD_PINS])
+def test_gqa_backward_pin(name, pin):
+    pin(naive.backward)
+
+
+def test_causal_rejects_more_queries_than_keys():
+    with pytest.raises(ValueError):
+        naive.causal_mask(5, 4)
 
 
 def test_softmax_rows_worked_example():
