@@ -9,6 +9,9 @@ missing, every call raises.
     import torch, exact_tiled_attention_forward_amd as fa
     o, lse = fa.fa_forward(q, k, v, causal=True)              # (B, H, N, d) bf16/fp16/fp32
     dq, dk, dv = fa.fa_backward(q, k, v, o, do, lse, causal=True)
+
+k and v may have fewer heads than q (grouped heads) and another length (cross-attention,
+a cached K/V); see ``fa_forward``.
 """
 
 from __future__ import annotations
@@ -57,6 +60,14 @@ def library() -> ctypes.CDLL:
     lib.fa_backward_dq.restype = i
     lib.fa_backward_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
     lib.fa_backward_dkdv.restype = i
+    lib.fa_forward_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_forward_ex.restype = i
+    lib.fa_backward_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_backward_ex.restype = i
+    lib.fa_backward_dq_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_backward_dq_ex.restype = i
+    lib.fa_backward_dkdv_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_backward_dkdv_ex.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -89,97 +100,114 @@ def _stream(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _shapes(q, k):
+    """(B, Hq, Hkv, Nq, Nk, d) from q (B, Hq, Nq, d) and k (B, Hkv, Nk, d)."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be 4-D: (B, H, N, d)")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if Bk != B or dk != d:
+        raise ValueError(f"k must be (B={B}, H_kv, N_k, d={d}) (got {tuple(k.shape)})")
+    return B, Hq, Hkv, Nq, Nk, d
+
+
 def fa_forward(q, k, v, o=None, lse=None, *, scale=None, causal=False, stream=None):
-    """O, lse = attention(q, k, v); tensors (B, H, N, d), lse (B, H, N) float32."""
+    """O, lse = attention(q, k, v).
+
+    q (B, Hq, Nq, d); k, v (B, Hkv, Nk, d) with Hq a multiple of Hkv (query head h
+    reads key/value head h // (Hq // Hkv)); o like q; lse (B, Hq, Nq) float32.  With
+    causal=True the queries are the last Nq positions of the Nk keys.
+    """
     lib = library()
-    if q.dim() != 4:
-        raise ValueError("q must be (B, H, N, d)")
-    B, H, N, d = q.shape
+    B, Hq, Hkv, Nq, Nk, d = _shapes(q, k)
     dt = q.dtype
     if dt not in _DTYPE_CODE:
         raise ValueError(f"unsupported dtype {dt}")
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
     pq = _gpu_tensor("q", q, dt)
-    pk = _gpu_tensor("k", k, dt, q.shape)
-    pv = _gpu_tensor("v", v, dt, q.shape)
+    pk = _gpu_tensor("k", k, dt)
+    pv = _gpu_tensor("v", v, dt, k.shape)
     po = _gpu_tensor("o", o, dt, q.shape)
-    pl = _gpu_tensor("lse", lse, torch.float32, (B, H, N))
+    pl = _gpu_tensor("lse", lse, torch.float32, (B, Hq, Nq))
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    _check(lib.fa_forward(pq, pk, pv, po, pl, B, H, N, d, ctypes.c_float(sc), int(bool(causal)),
-                          _DTYPE_CODE[dt], _stream(stream, q.device)))
+    _check(lib.fa_forward_ex(pq, pk, pv, po, pl, B, Hq, Hkv, Nq, Nk, d, ctypes.c_float(sc), int(bool(causal)),
+                             _DTYPE_CODE[dt], _stream(stream, q.device)))
     return o, lse
 
 
 def fa_backward_workspace_bytes(B, H, N, d):
+    """Workspace bytes of the backward for B batches, H query heads and N query rows."""
     return int(library().fa_backward_workspace_bytes(B, H, N, d))
+
+
+def _workspace(q, workspace):
+    B, Hq, Nq, d = q.shape
+    if workspace is None:
+        workspace = torch.empty(max(fa_backward_workspace_bytes(B, Hq, Nq, d), 16), dtype=torch.uint8, device=q.device)
+    return workspace
 
 
 def fa_backward(q, k, v, o, do, lse, dq=None, dk=None, dv=None, *, scale=None, causal=False,
                 workspace=None, stream=None):
-    """dQ, dK, dV (float32, (B, H, N, d)) of sum(O * dO), recomputing P from q, k and lse."""
+    """dQ (like q), dK, dV (like k) as float32 gradients of sum(O * dO), recomputing P from
+    q, k and lse.  Shapes and grouping as for fa_forward."""
     lib = library()
-    B, H, N, d = q.shape
-    dt = q.dtype
+    B, Hq, Hkv, Nq, Nk, d = _shapes(q, k)
+    dt, f32 = q.dtype, torch.float32
     if dt not in _DTYPE_CODE:
         raise ValueError(f"unsupported dtype {dt}")
-    f32 = torch.float32
     dq = torch.empty(q.shape, dtype=f32, device=q.device) if dq is None else dq
-    dk = torch.empty(q.shape, dtype=f32, device=q.device) if dk is None else dk
-    dv = torch.empty(q.shape, dtype=f32, device=q.device) if dv is None else dv
-    need = fa_backward_workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    ptrs = [_gpu_tensor("q", q, dt), _gpu_tensor("k", k, dt, q.shape), _gpu_tensor("v", v, dt, q.shape),
+    dk = torch.empty(k.shape, dtype=f32, device=q.device) if dk is None else dk
+    dv = torch.empty(k.shape, dtype=f32, device=q.device) if dv is None else dv
+    workspace = _workspace(q, workspace)
+    ptrs = [_gpu_tensor("q", q, dt), _gpu_tensor("k", k, dt), _gpu_tensor("v", v, dt, k.shape),
             _gpu_tensor("o", o, dt, q.shape), _gpu_tensor("do", do, dt, q.shape),
-            _gpu_tensor("lse", lse, f32, (B, H, N)), _gpu_tensor("dq", dq, f32, q.shape),
-            _gpu_tensor("dk", dk, f32, q.shape), _gpu_tensor("dv", dv, f32, q.shape),
+            _gpu_tensor("lse", lse, f32, (B, Hq, Nq)), _gpu_tensor("dq", dq, f32, q.shape),
+            _gpu_tensor("dk", dk, f32, k.shape), _gpu_tensor("dv", dv, f32, k.shape),
             _gpu_tensor("workspace", workspace)]
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    _check(lib.fa_backward(*ptrs, workspace.numel() * workspace.element_size(), B, H, N, d,
-                           ctypes.c_float(sc), int(bool(causal)), _DTYPE_CODE[dt], _stream(stream, q.device)))
+    _check(lib.fa_backward_ex(*ptrs, workspace.numel() * workspace.element_size(), B, Hq, Hkv, Nq, Nk, d,
+                              ctypes.c_float(sc), int(bool(causal)), _DTYPE_CODE[dt], _stream(stream, q.device)))
     return dq, dk, dv
-
-
-def _bwd_common(q, workspace):
-    B, H, N, d = q.shape
-    if q.dtype not in _DTYPE_CODE:
-        raise ValueError(f"unsupported dtype {q.dtype}")
-    need = fa_backward_workspace_bytes(B, H, N, d)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    return B, H, N, d, workspace
 
 
 def fa_backward_dq(q, k, v, do, lse, dq=None, *, scale=None, causal=False, workspace=None, stream=None):
     """First backward stage: dQ, plus D and lse*log2(e) in ``workspace`` (returned) for
     fa_backward_dkdv."""
     lib = library()
-    B, H, N, d, workspace = _bwd_common(q, workspace)
+    B, Hq, Hkv, Nq, Nk, d = _shapes(q, k)
     dt, f32 = q.dtype, torch.float32
+    if dt not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {dt}")
+    workspace = _workspace(q, workspace)
     dq = torch.empty(q.shape, dtype=f32, device=q.device) if dq is None else dq
-    ptrs = [_gpu_tensor("q", q, dt), _gpu_tensor("k", k, dt, q.shape), _gpu_tensor("v", v, dt, q.shape),
-            _gpu_tensor("do", do, dt, q.shape), _gpu_tensor("lse", lse, f32, (B, H, N)),
+    ptrs = [_gpu_tensor("q", q, dt), _gpu_tensor("k", k, dt), _gpu_tensor("v", v, dt, k.shape),
+            _gpu_tensor("do", do, dt, q.shape), _gpu_tensor("lse", lse, f32, (B, Hq, Nq)),
             _gpu_tensor("dq", dq, f32, q.shape), _gpu_tensor("workspace", workspace)]
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    _check(lib.fa_backward_dq(*ptrs, workspace.numel() * workspace.element_size(), B, H, N, d,
-                              ctypes.c_float(sc), int(bool(causal)), _DTYPE_CODE[dt], _stream(stream, q.device)))
+    _check(lib.fa_backward_dq_ex(*ptrs, workspace.numel() * workspace.element_size(), B, Hq, Hkv, Nq, Nk, d,
+                                 ctypes.c_float(sc), int(bool(causal)), _DTYPE_CODE[dt], _stream(stream, q.device)))
     return dq, workspace
 
 
 def fa_backward_dkdv(q, k, v, do, workspace, dk=None, dv=None, *, scale=None, causal=False, stream=None):
     """Second backward stage: dK, dV from the workspace fa_backward_dq filled."""
     lib = library()
-    B, H, N, d, workspace = _bwd_common(q, workspace)
+    B, Hq, Hkv, Nq, Nk, d = _shapes(q, k)
     dt, f32 = q.dtype, torch.float32
-    dk = torch.empty(q.shape, dtype=f32, device=q.device) if dk is None else dk
-    dv = torch.empty(q.shape, dtype=f32, device=q.device) if dv is None else dv
-    ptrs = [_gpu_tensor("q", q, dt), _gpu_tensor("k", k, dt, q.shape), _gpu_tensor("v", v, dt, q.shape),
-            _gpu_tensor("do", do, dt, q.shape), _gpu_tensor("dk", dk, f32, q.shape),
-            _gpu_tensor("dv", dv, f32, q.shape), _gpu_tensor("workspace", workspace)]
+    if dt not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {dt}")
+    if workspace is None:
+        raise ValueError("fa_backward_dkdv needs the workspace fa_backward_dq filled")
+    dk = torch.empty(k.shape, dtype=f32, device=q.device) if dk is None else dk
+    dv = torch.empty(k.shape, dtype=f32, device=q.device) if dv is None else dv
+    ptrs = [_gpu_tensor("q", q, dt), _gpu_tensor("k", k, dt), _gpu_tensor("v", v, dt, k.shape),
+            _gpu_tensor("do", do, dt, q.shape), _gpu_tensor("dk", dk, f32, k.shape),
+            _gpu_tensor("dv", dv, f32, k.shape), _gpu_tensor("workspace", workspace)]
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    _check(lib.fa_backward_dkdv(*ptrs, workspace.numel() * workspace.element_size(), B, H, N, d,
-                                ctypes.c_float(sc), int(bool(causal)), _DTYPE_CODE[dt], _stream(stream, q.device)))
+    _check(lib.fa_backward_dkdv_ex(*ptrs, workspace.numel() * workspace.element_size(), B, Hq, Hkv, Nq, Nk, d,
+                                   ctypes.c_float(sc), int(bool(causal)), _DTYPE_CODE[dt], _stream(stream, q.device)))
     return dk, dv

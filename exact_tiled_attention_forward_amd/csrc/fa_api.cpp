@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -24,17 +24,19 @@ int elem_size(int dtype) {
 }
 
 // Shape checks shared by forward and backward.
-int check_shape(int B, int H, int N, int d, int dtype) {
-  if (B < 1 || H < 1 || N < 1) return FA_ERR_SHAPE;
+int check_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d, int dtype, int causal) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (causal && Nq > Nk) return FA_ERR_SHAPE;  // rows with no visible key
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   const int es = elem_size(dtype);
   if (es == 0) return FA_ERR_UNSUPPORTED;
   // one head of a tensor addressed with 32-bit byte offsets (fp32 gradients: 4 bytes)
-  if ((int64_t)N * d * 4 >= (int64_t)1 << 31) return FA_ERR_SHAPE;
-  // grid: B*H*ceil(N/32) workgroups at most
-  const int64_t groups = (int64_t)B * H * ((N + 31) / 32);
-  if (groups >= (int64_t)1 << 31) return FA_ERR_SHAPE;
-  if ((int64_t)B * H >= (int64_t)1 << 30) return FA_ERR_SHAPE;
+  if ((int64_t)Nq * d * 4 >= (int64_t)1 << 31 || (int64_t)Nk * d * 4 >= (int64_t)1 << 31) return FA_ERR_SHAPE;
+  // grids: B*Hq*ceil(Nq/32) and B*Hkv*ceil(Nk/32) workgroups at most
+  if ((int64_t)B * Hq * ((Nq + 31) / 32) >= (int64_t)1 << 31) return FA_ERR_SHAPE;
+  if ((int64_t)B * Hkv * ((Nk + 31) / 32) >= (int64_t)1 << 31) return FA_ERR_SHAPE;
+  if ((int64_t)B * Hq >= (int64_t)1 << 30) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -47,18 +49,23 @@ int check_scale(float scale) {
 
 extern "C" {
 
-int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
-               float scale, int causal, fa_dtype_t dtype, hipStream_t stream) {
+int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
+                  int Nk, int d, float scale, int causal, fa_dtype_t dtype, hipStream_t stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  int st = check_shape(B, H, N, d, (int)dtype);
+  int st = check_shape(B, Hq, Hkv, Nq, Nk, d, (int)dtype, causal);
   if (st != FA_OK) return st;
   if ((st = check_scale(scale)) != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse)) return FA_ERR_ALIGN;
 
-  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal != 0, (int)dtype, stream};
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal != 0, (int)dtype, stream};
   (void)hipGetLastError();  // clear a pending error so the check below is about this launch
   if (fa::launch_forward(a) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
+}
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
+               float scale, int causal, fa_dtype_t dtype, hipStream_t stream) {
+  return fa_forward_ex(q, k, v, o, lse, B, H, H, N, N, d, scale, causal, dtype, stream);
 }
 
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
@@ -73,24 +80,24 @@ namespace {
 // as a valid stand-in (q) by the caller of this helper.
 int check_backward(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
                    const float* dq, const float* dk, const float* dv, const void* workspace, size_t workspace_bytes,
-                   int B, int H, int N, int d, float scale, fa_dtype_t dtype) {
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, fa_dtype_t dtype) {
   if (!q || !k || !v || !o || !dO || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
-  int st = check_shape(B, H, N, d, (int)dtype);
+  int st = check_shape(B, Hq, Hkv, Nq, Nk, d, (int)dtype, causal);
   if (st != FA_OK) return st;
   if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   if ((st = check_scale(scale)) != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned16(dq) ||
       !aligned16(dk) || !aligned16(dv) || !aligned4(lse))
     return FA_ERR_ALIGN;
-  if (!workspace || workspace_bytes < fa_backward_workspace_bytes(B, H, N, d)) return FA_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < fa_backward_workspace_bytes(B, Hq, Nq, d)) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
   return FA_OK;
 }
 
 int run_backward(const void* q, const void* k, const void* v, const void* dO, const float* lse, float* dq,
-                 float* dk, float* dv, void* workspace, int B, int H, int N, int d, float scale, int causal,
-                 fa_dtype_t dtype, hipStream_t stream, int stages) {
-  fa::BwdArgs a{q, k, v, nullptr, dO, lse, dq, dk, dv, (float*)workspace, B, H, N, d, scale, causal != 0,
+                 float* dk, float* dv, void* workspace, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                 int causal, fa_dtype_t dtype, hipStream_t stream, int stages) {
+  fa::BwdArgs a{q, k, v, nullptr, dO, lse, dq, dk, dv, (float*)workspace, B, Hq, Hkv, Nq, Nk, d, scale, causal != 0,
                 (int)dtype, stream};
   (void)hipGetLastError();
   if (fa::launch_backward(a, stages) != hipSuccess) return FA_ERR_HIP;
@@ -99,40 +106,66 @@ int run_backward(const void* q, const void* k, const void* v, const void* dO, co
 
 }  // namespace
 
+int fa_backward_ex(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                   float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                   int Nq, int Nk, int d, float scale, int causal, fa_dtype_t dtype, hipStream_t stream) {
+  const int st = check_backward(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, d,
+                                scale, causal, dtype);
+  if (st != FA_OK) return st;
+  return run_backward(q, k, v, dO, lse, dq, dk, dv, workspace, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, stream,
+                      fa::kStageDq | fa::kStageDkdv);
+}
+
+int fa_backward_dq_ex(const void* q, const void* k, const void* v, const void* dO, const float* lse, float* dq,
+                      void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                      float scale, int causal, fa_dtype_t dtype, hipStream_t stream) {
+  const float* f = (const float*)q;  // stand-in for the gradients this stage does not touch
+  const int st = check_backward(q, k, v, q, dO, lse, dq, f, f, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, d,
+                                scale, causal, dtype);
+  if (st != FA_OK) return st;
+  return run_backward(q, k, v, dO, lse, dq, nullptr, nullptr, workspace, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype,
+                      stream, fa::kStageDq);
+}
+
+int fa_backward_dkdv_ex(const void* q, const void* k, const void* v, const void* dO, float* dk, float* dv,
+                        const void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                        float scale, int causal, fa_dtype_t dtype, hipStream_t stream) {
+  const float* f = (const float*)q;
+  const int st = check_backward(q, k, v, q, dO, f, f, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, d,
+                                scale, causal, dtype);
+  if (st != FA_OK) return st;
+  return run_backward(q, k, v, dO, nullptr, nullptr, dk, dv, const_cast<void*>(workspace), B, Hq, Hkv, Nq, Nk, d,
+                      scale, causal, dtype, stream, fa::kStageDkdv);
+}
+
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
                 float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes, int B, int H, int N,
                 int d, float scale, int causal, fa_dtype_t dtype, hipStream_t stream) {
-  const int st = check_backward(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, H, N, d, scale, dtype);
-  if (st != FA_OK) return st;
-  return run_backward(q, k, v, dO, lse, dq, dk, dv, workspace, B, H, N, d, scale, causal, dtype, stream,
-                      fa::kStageDq | fa::kStageDkdv);
+  return fa_backward_ex(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, H, H, N, N, d, scale, causal,
+                        dtype, stream);
 }
 
 int fa_backward_dq(const void* q, const void* k, const void* v, const void* dO, const float* lse, float* dq,
                    void* workspace, size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
                    fa_dtype_t dtype, hipStream_t stream) {
-  const float* f = (const float*)q;  // stand-in for the gradients this stage does not touch
-  const int st = check_backward(q, k, v, q, dO, lse, dq, f, f, workspace, workspace_bytes, B, H, N, d, scale, dtype);
-  if (st != FA_OK) return st;
-  return run_backward(q, k, v, dO, lse, dq, nullptr, nullptr, workspace, B, H, N, d, scale, causal, dtype, stream,
-                      fa::kStageDq);
+  return fa_backward_dq_ex(q, k, v, dO, lse, dq, workspace, workspace_bytes, B, H, H, N, N, d, scale, causal, dtype,
+                           stream);
 }
 
 int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dO, float* dk, float* dv,
                      const void* workspace, size_t workspace_bytes, int B, int H, int N, int d, float scale,
                      int causal, fa_dtype_t dtype, hipStream_t stream) {
-  const float* f = (const float*)q;
-  const int st = check_backward(q, k, v, q, dO, f, f, dk, dv, workspace, workspace_bytes, B, H, N, d, scale, dtype);
-  if (st != FA_OK) return st;
-  return run_backward(q, k, v, dO, nullptr, nullptr, dk, dv, const_cast<void*>(workspace), B, H, N, d, scale,
-                      causal, dtype, stream, fa::kStageDkdv);
+  return fa_backward_dkdv_ex(q, k, v, dO, dk, dv, workspace, workspace_bytes, B, H, H, N, N, d, scale, causal, dtype,
+                             stream);
 }
 
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
-    case FA_ERR_SHAPE: return "B, H or N < 1, or a tensor is too large for the kernels' 32-bit offsets";
+    case FA_ERR_SHAPE:
+      return "a size < 1, Hq not a multiple of Hkv, causal with Nq > Nk, or a tensor too large for the kernels' "
+             "32-bit offsets";
     case FA_ERR_UNSUPPORTED: return "unsupported head dimension (d must be 64 or 128), dtype, or fp32 backward";
     case FA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned (lse: 4-byte)";
     case FA_ERR_WORKSPACE: return "backward workspace is NULL or smaller than fa_backward_workspace_bytes()";

@@ -40,7 +40,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                                                          const uint16_t* __restrict__ V,
                                                          const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
                                                          float* __restrict__ delta, float* __restrict__ lse2,
-                                                         float* __restrict__ dQ, int BH, int N, float c, float scale) {
+                                                         float* __restrict__ dQ, int BH, int G, int Nq, int Nk,
+                                                         float c, float scale) {
   constexpr int BR = 32 * NW;
   constexpr int NT = NW * 64;
   constexpr int TB = BC * D * 2;
@@ -51,23 +52,24 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   FA_LDS uint8_t* lds = (FA_LDS uint8_t*)(smem);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, c32 = lane & 31;
-  const int nqb = (N + BR - 1) / BR;
-  const int bh = blockIdx.x % BH;
+  const int nqb = (Nq + BR - 1) / BR;
+  const int bh = blockIdx.x % BH;  // query head; it reads key/value head bh / G
   int qb = blockIdx.x / BH;
   if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
   const int q0 = qb * BR;
   const int qw0 = q0 + 32 * wave;
   const int qrow = qw0 + c32;
 
-  const size_t head = (size_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const auto rq = make_rsrc(Q + head, head_bytes);
-  const auto rk = make_rsrc(K + head, head_bytes);
-  const auto rv = make_rsrc(V + head, head_bytes);
-  const auto rdo = make_rsrc(dO + head, head_bytes);
+  const size_t head = (size_t)bh * Nq * D;
+  const size_t kvhead = (size_t)(bh / G) * Nk * D;
+  const int off = Nk - Nq;  // causal: query row i sees keys j <= i + off
+  const auto rq = make_rsrc(Q + head, (uint32_t)Nq * D * 2);
+  const auto rk = make_rsrc(K + kvhead, (uint32_t)Nk * D * 2);
+  const auto rv = make_rsrc(V + kvhead, (uint32_t)Nk * D * 2);
+  const auto rdo = make_rsrc(dO + head, (uint32_t)Nq * D * 2);
 
-  const int nkt_all = (N + BC - 1) / BC;
-  const int nkt = CAUSAL ? min(nkt_all, (q0 + BR - 1) / BC + 1) : nkt_all;
+  const int nkt_all = (Nk + BC - 1) / BC;
+  const int nkt = CAUSAL ? min(nkt_all, (q0 + BR - 1 + off) / BC + 1) : nkt_all;
 
   u32x4 qf[DS], of[DS];
 #pragma unroll
@@ -75,8 +77,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     qf[st] = buffer_load16(rq, qrow * (D * 2) + ((2 * st + half) << 4));
     of[st] = buffer_load16(rdo, qrow * (D * 2) + ((2 * st + half) << 4));
   }
-  const bool qvalid = qrow < N;
-  const float l2 = qvalid ? LSE[(size_t)bh * N + qrow] * kLog2e : 0.f;
+  const bool qvalid = qrow < Nq;
+  const float l2 = qvalid ? LSE[(size_t)bh * Nq + qrow] * kLog2e : 0.f;
 
   float dsum = 0.f;  // pass 1: this half's part of D_i = sum_j P_ij dP_ij
   float dl = 0.f;    // pass 2: D_i
@@ -97,10 +99,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         tile_load_async<D, BC, NT>(lds + (2 + (cur ^ 1)) * TB, rv, (j + 1) * BC, tid);
       }
       const int k0 = j * BC;
-      if (CAUSAL && k0 > qw0 + 31) continue;
+      if (CAUSAL && k0 > qw0 + 31 + off) continue;
       const FA_LDS uint8_t* kt = lds + cur * TB;
       const FA_LDS uint8_t* vt = lds + (2 + cur) * TB;
-      const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw0);
+      const bool need_mask = (k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw0 + off);
 
       uint32_t sh[KB][8], sl[KB][8];
 #pragma unroll
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
           float p = fast_exp2(fmaf(s[i], c, -l2));
           if (need_mask) {
             const int key = k0 + 32 * kb + acc_row(i, half);
-            if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
+            if (key >= Nk || (CAUSAL && key > qrow + off)) p = 0.f;
           }
           if (pass == 0) dsum = fmaf(p, dp[i], dsum);
           else dp[i] = p * (dp[i] - dl);
@@ -145,8 +147,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (pass == 0) {
       dl = sum_halves(dsum);
       if (qvalid && half == 0) {
-        delta[(size_t)bh * N + qrow] = dl;
-        lse2[(size_t)bh * N + qrow] = l2;
+        delta[(size_t)bh * Nq + qrow] = dl;
+        lse2[(size_t)bh * Nq + qrow] = l2;
       }
     }
   }
@@ -182,7 +184,7 @@ template <class T, int D, int NP, int BQ, bool CAUSAL>
 __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ delta, const float* __restrict__ lse2,
-    float* __restrict__ dK, float* __restrict__ dV, int BH, int N, float c, float scale) {
+    float* __restrict__ dK, float* __restrict__ dV, int BHkv, int G, int Nq, int Nk, float c, float scale) {
   constexpr int NW = 2 * NP;
   constexpr int BKV = 32 * NP;
   constexpr int NT = NW * 64;
@@ -202,27 +204,31 @@ __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(2, 
   const bool role_b = wave >= NP;
   const int pair = role_b ? wave - NP : wave;
   FA_LDS f32x4* pex = (FA_LDS f32x4*)(smem + 4 * TB + 2 * 2 * 64 * 4 + pair * PB);
-  const int bh = blockIdx.x % BH;
-  const int kblk = blockIdx.x / BH;  // causal: block 0 sees the most queries and starts first
+  const int bkv = blockIdx.x % BHkv;  // key/value head; its query heads are bkv*G .. bkv*G + G-1
+  const int kblk = blockIdx.x / BHkv;  // causal: block 0 sees the most queries and starts first
   const int k0 = kblk * BKV;
   const int kw0 = k0 + 32 * pair;
   const int krow = kw0 + c32;
 
-  const size_t head = (size_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const auto rq = make_rsrc(Q + head, head_bytes);
-  const auto rdo = make_rsrc(dO + head, head_bytes);
-  const auto rl = make_rsrc(lse2 + (size_t)bh * N, (uint32_t)N * 4);
-  const auto rd = make_rsrc(delta + (size_t)bh * N, (uint32_t)N * 4);
+  const size_t kvhead = (size_t)bkv * Nk * D;
+  const int off = Nk - Nq;  // causal: query row i sees keys j <= i + off
 
-  const int nqt = (N + BQ - 1) / BQ;
-  const int qt0 = CAUSAL ? (k0 / BQ) : 0;  // earlier query tiles see none of these keys
+  const int nqt = (Nq + BQ - 1) / BQ;
+  const int qt0 = CAUSAL ? max(k0 - off, 0) / BQ : 0;  // earlier query tiles see none of these keys
+  const int nt = nqt - qt0;                             // query tiles per query head of the group
+  const int ntiles = G * nt;
 
-  auto load_tile = [&](int qt, int buf) {
-    tile_load_async<D, BQ, NT>(lds + buf * TB, rq, qt * BQ, tid);
-    tile_load_async<D, BQ, NT>(lds + (2 + buf) * TB, rdo, qt * BQ, tid);
+  // streamed tile t: query tile qt0 + t % nt of query head bkv*G + t / nt
+  auto load_tile = [&](int t, int buf) {
+    const int bhq = bkv * G + t / nt;
+    const int qt = qt0 + t % nt;
+    const size_t qhead = (size_t)bhq * Nq * D;
+    tile_load_async<D, BQ, NT>(lds + buf * TB, make_rsrc(Q + qhead, (uint32_t)Nq * D * 2), qt * BQ, tid);
+    tile_load_async<D, BQ, NT>(lds + (2 + buf) * TB, make_rsrc(dO + qhead, (uint32_t)Nq * D * 2), qt * BQ, tid);
     if (wave == 0) {
       // 64 floats of lse2 and of delta from the tile's first query (the first BQ used)
+      const auto rl = make_rsrc(lse2 + (size_t)bhq * Nq, (uint32_t)Nq * 4);
+      const auto rd = make_rsrc(delta + (size_t)bhq * Nq, (uint32_t)Nq * 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (FA_LDS void*)(stats + buf * 128), 4, (qt * BQ + lane) * 4, 0,
                                                0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (FA_LDS void*)(stats + buf * 128 + 64), 4,
@@ -230,12 +236,12 @@ __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(2, 
     }
   };
 
-  if (qt0 < nqt) load_tile(qt0, 0);
+  if (ntiles > 0) load_tile(0, 0);
 
   // this wave's keys (A) or values (B) as B operands (lane = key, 8 consecutive d per lane)
   u32x4 kv[DS];
   {
-    const auto rkv = make_rsrc((role_b ? V : K) + head, head_bytes);
+    const auto rkv = make_rsrc((role_b ? V : K) + kvhead, (uint32_t)Nk * D * 2);
 #pragma unroll
     for (int st = 0; st < DS; ++st) kv[st] = buffer_load16(rkv, krow * (D * 2) + ((2 * st + half) << 4));
   }
@@ -244,20 +250,20 @@ __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = (f32x16){};
 
-  for (int qt = qt0; qt < nqt; ++qt) {
+  for (int t = 0; t < ntiles; ++t) {
     wait_vmem();
     __syncthreads();
-    const int cur = (qt - qt0) & 1;
-    if (qt + 1 < nqt) load_tile(qt + 1, cur ^ 1);
-    const int q0 = qt * BQ;
+    const int cur = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1, cur ^ 1);
+    const int q0 = (qt0 + t % nt) * BQ;
     // every query of the tile precedes this pair's keys: P = 0 (both waves of the pair
     // agree, and both still meet the barrier below)
-    const bool active = !(CAUSAL && q0 + BQ - 1 < kw0);
+    const bool active = !(CAUSAL && q0 + BQ - 1 + off < kw0);
     const FA_LDS uint8_t* qtile = lds + cur * TB;
     const FA_LDS uint8_t* otile = lds + (2 + cur) * TB;
     const FA_LDS float* l2 = stats + cur * 128;
     const FA_LDS float* dl = l2 + 64;
-    const bool need_mask = (q0 + BQ > N) || (CAUSAL && q0 < kw0 + 31);
+    const bool need_mask = (q0 + BQ > Nq) || (CAUSAL && q0 + off < kw0 + 31);
 
     // phase 1: A computes P and publishes it, B computes dP
     f32x16 x[QB];  // A: P, B: dP (rows = queries q0 + 32*qb + acc_row(i, half))
@@ -282,7 +288,7 @@ __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(2, 
               float p = fast_exp2(fmaf(x[qb][i], c, -lv[e]));
               if (need_mask) {
                 const int q = q0 + r0 + e;
-                if (q >= N || (CAUSAL && krow > q)) p = 0.f;
+                if (q >= Nq || (CAUSAL && krow > q + off)) p = 0.f;
               }
               x[qb][i] = p;
             }
@@ -327,8 +333,8 @@ __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(2, 
   }
 
   // lane = key (column of dK^T / dV^T), registers = head-dimension rows
-  if (krow < N) {
-    float* out = (role_b ? dK : dV) + head + (size_t)krow * D;
+  if (krow < Nk) {
+    float* out = (role_b ? dK : dV) + kvhead + (size_t)krow * D;
     const float f = role_b ? scale : 1.0f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -353,26 +359,28 @@ constexpr int kBQkv = 64;
 
 template <class T, int D, bool CAUSAL>
 hipError_t go(const BwdArgs& a, int stages) {
-  const int BH = a.B * a.H;
-  const long rows = (long)BH * a.N;
+  const int BHq = a.B * a.Hq;
+  const int BHkv = a.B * a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const long rows = (long)BHq * a.Nq;
   float* delta = a.delta;
   float* lse2 = a.delta + rows;
   const float c = a.scale * kLog2e;
   if (stages & kStageDq) {
     constexpr int BR = 32 * kNWq;
-    const int nqb = (a.N + BR - 1) / BR;
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, kNWq, kBCq, CAUSAL>), dim3(BH * nqb), dim3(kNWq * 64), 0, a.stream,
+    const int nqb = (a.Nq + BR - 1) / BR;
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, kNWq, kBCq, CAUSAL>), dim3(BHq * nqb), dim3(kNWq * 64), 0, a.stream,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO,
-                       a.lse, delta, lse2, a.dq, BH, a.N, c, a.scale);
+                       a.lse, delta, lse2, a.dq, BHq, G, a.Nq, a.Nk, c, a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & kStageDkdv) {
     constexpr int BKV = 32 * kNPkv;
-    const int nkb = (a.N + BKV - 1) / BKV;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kNPkv, kBQkv, CAUSAL>), dim3(BH * nkb), dim3(2 * kNPkv * 64), 0,
+    const int nkb = (a.Nk + BKV - 1) / BKV;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kNPkv, kBQkv, CAUSAL>), dim3(BHkv * nkb), dim3(2 * kNPkv * 64), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dO, delta, lse2, a.dk, a.dv, BH, a.N, c, a.scale);
+                       (const uint16_t*)a.dO, delta, lse2, a.dk, a.dv, BHkv, G, a.Nq, a.Nk, c, a.scale);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -50,7 +50,7 @@ constexpr float kRescaleSlack = 8.0f;
 template <class T, int D, int NW, int BC, int WPE, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void fwd16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int N, float c) {
+    uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int G, int Nq, int Nk, float c) {
   constexpr int BR = 32 * NW;
   constexpr int NT = NW * 64;
   constexpr int TB = BC * D * 2;  // bytes of one K or V tile
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   FA_LDS uint8_t* lds = (FA_LDS uint8_t*)(smem);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, c32 = lane & 31;
-  const int nqb = (N + BR - 1) / BR;
+  const int nqb = (Nq + BR - 1) / BR;
   const int bh = blockIdx.x % BH;
   int qb = blockIdx.x / BH;
   if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
@@ -70,14 +70,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const int qw0 = q0 + 32 * wave;
   const int qrow = qw0 + c32;
 
-  const size_t head = (size_t)bh * N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const auto rq = make_rsrc(Q + head, head_bytes);
-  const auto rk = make_rsrc(K + head, head_bytes);
-  const auto rv = make_rsrc(V + head, head_bytes);
+  // query head bh reads key/value head bh / G; causal: query row i sits at position
+  // i + off of the key sequence and sees keys j <= i + off
+  const size_t head = (size_t)bh * Nq * D;
+  const size_t kvhead = (size_t)(bh / G) * Nk * D;
+  const int off = Nk - Nq;
+  const auto rq = make_rsrc(Q + head, (uint32_t)Nq * D * 2);
+  const auto rk = make_rsrc(K + kvhead, (uint32_t)Nk * D * 2);
+  const auto rv = make_rsrc(V + kvhead, (uint32_t)Nk * D * 2);
 
-  const int nkt_all = (N + BC - 1) / BC;
-  const int nkt = CAUSAL ? min(nkt_all, (q0 + BR - 1) / BC + 1) : nkt_all;
+  const int nkt_all = (Nk + BC - 1) / BC;
+  const int nkt = CAUSAL ? min(nkt_all, (q0 + BR - 1 + off) / BC + 1) : nkt_all;
 
   tile_load_async<D, BC, NT>(lds, rk, 0, tid);
   tile_load_async<D, BC, NT>(lds + 2 * TB, rv, 0, tid);
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       tile_load_async<D, BC, NT>(lds + (2 + (cur ^ 1)) * TB, rv, (j + 1) * BC, tid);
     }
     const int k0 = j * BC;
-    if (CAUSAL && k0 > qw0 + 31) continue;  // every key of the tile is in this wave's future
+    if (CAUSAL && k0 > qw0 + 31 + off) continue;  // every key of the tile is in this wave's future
     const FA_LDS uint8_t* kt = lds + cur * TB;
     const FA_LDS uint8_t* vt = lds + (2 + cur) * TB;
 
@@ -117,13 +120,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     }
 
     // masks: keys past the end, and (causal) keys after the query
-    if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw0)) {
+    if ((k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw0 + off)) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + 32 * kb + acc_row(i, half);
-          s[kb][i] = (key >= N || (CAUSAL && key > qrow)) ? -INFINITY : s[kb][i];
+          s[kb][i] = (key >= Nk || (CAUSAL && key > qrow + off)) ? -INFINITY : s[kb][i];
         }
     }
 
@@ -173,7 +176,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   // average of V rows; the logsumexp uses the fp32 sum.
   const float lt = sum_halves(l);
   const float inv = 1.0f / sum_halves(lr);
-  if (qrow < N) {
+  if (qrow < Nq) {
     uint16_t* orow = O + head + (size_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         w.y = T::pack(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
         *(u32x2*)(orow + d) = w;
       }
-    if (half == 0) LSE[(size_t)bh * N + qrow] = (m + log2f(lt)) * kLn2;
+    if (half == 0) LSE[(size_t)bh * Nq + qrow] = (m + log2f(lt)) * kLn2;
   }
 }
 
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 template <int D, int NW, int BC, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                         const float* __restrict__ V, float* __restrict__ O,
-                                                        float* __restrict__ LSE, int BH, int N, float c) {
+                                                        float* __restrict__ LSE, int BH, int G, int Nq, int Nk, float c) {
   constexpr int BR = 32 * NW;
   constexpr int NT = NW * 64;
   constexpr int KS = D + 2, VS = D + 8;
@@ -207,17 +210,19 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
   __shared__ __attribute__((aligned(16))) float vs_[BC * VS];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, c32 = lane & 31;
-  const int nqb = (N + BR - 1) / BR;
+  const int nqb = (Nq + BR - 1) / BR;
   const int bh = blockIdx.x % BH;
   int qb = blockIdx.x / BH;
   if (CAUSAL) qb = nqb - 1 - qb;
   const int q0 = qb * BR;
   const int qw0 = q0 + 32 * wave;
   const int qrow = qw0 + c32;
-  const size_t head = (size_t)bh * N * D;
-  const auto rq = make_rsrc(Q + head, (uint32_t)N * D * 4);
-  const auto rk = make_rsrc(K + head, (uint32_t)N * D * 4);
-  const auto rv = make_rsrc(V + head, (uint32_t)N * D * 4);
+  const size_t head = (size_t)bh * Nq * D;
+  const size_t kvhead = (size_t)(bh / G) * Nk * D;
+  const int off = Nk - Nq;
+  const auto rq = make_rsrc(Q + head, (uint32_t)Nq * D * 4);
+  const auto rk = make_rsrc(K + kvhead, (uint32_t)Nk * D * 4);
+  const auto rv = make_rsrc(V + kvhead, (uint32_t)Nk * D * 4);
 
   float qv[D / 2];  // this lane's query at d = 2*st + half
 #pragma unroll
@@ -232,8 +237,8 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
     for (int e = 0; e < 4; ++e) qv[4 * st + e] = half ? f[2 * e + 1] : f[2 * e];
   }
 
-  const int nkt_all = (N + BC - 1) / BC;
-  const int nkt = CAUSAL ? min(nkt_all, (q0 + BR - 1) / BC + 1) : nkt_all;
+  const int nkt_all = (Nk + BC - 1) / BC;
+  const int nkt = CAUSAL ? min(nkt_all, (q0 + BR - 1 + off) / BC + 1) : nkt_all;
   float m = -INFINITY, l = 0.f;
   f32x16 o[DB];
 #pragma unroll
@@ -253,7 +258,7 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
       *(u32x4*)(vs_ + r * VS + cc) = vw;
     }
     __syncthreads();
-    if (CAUSAL && k0 > qw0 + 31) continue;
+    if (CAUSAL && k0 > qw0 + 31 + off) continue;
 
     f32x16 s[KB];
 #pragma unroll
@@ -263,13 +268,13 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
       for (int st = 0; st < D / 2; ++st)
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(ks_[(32 * kb + c32) * KS + 2 * st + half], qv[st], s[kb], 0, 0, 0);
     }
-    if ((k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw0)) {
+    if ((k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw0 + off)) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + 32 * kb + acc_row(i, half);
-          if (key >= N || (CAUSAL && key > qrow)) s[kb][i] = -INFINITY;
+          if (key >= Nk || (CAUSAL && key > qrow + off)) s[kb][i] = -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -306,7 +311,7 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
 
   const float lt = sum_halves(l);
   const float inv = 1.0f / lt;
-  if (qrow < N) {
+  if (qrow < Nq) {
     float* orow = O + head + (size_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -316,7 +321,7 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
         *(f32x4*)(orow + d) = (f32x4){o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv,
                                       o[db][4 * g + 3] * inv};
       }
-    if (half == 0) LSE[(size_t)bh * N + qrow] = (m + log2f(lt)) * kLn2;
+    if (half == 0) LSE[(size_t)bh * Nq + qrow] = (m + log2f(lt)) * kLn2;
   }
 }
 
@@ -342,20 +347,20 @@ template <class T, int D, bool CAUSAL>
 hipError_t go16(const FwdArgs& a) {
   using S = Fwd16Shape<D>;
   constexpr int BR = 32 * S::NW;
-  const int nqb = (a.N + BR - 1) / BR;
-  hipLaunchKernelGGL((fwd16_kernel<T, D, S::NW, S::BC, S::WPE, CAUSAL>), dim3(a.B * a.H * nqb), dim3(S::NW * 64), 0,
+  const int nqb = (a.Nq + BR - 1) / BR;
+  hipLaunchKernelGGL((fwd16_kernel<T, D, S::NW, S::BC, S::WPE, CAUSAL>), dim3(a.B * a.Hq * nqb), dim3(S::NW * 64), 0,
                      a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                     a.B * a.H, a.N, a.scale * kLog2e);
+                     a.B * a.Hq, a.Hq / a.Hkv, a.Nq, a.Nk, a.scale * kLog2e);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 hipError_t go32(const FwdArgs& a) {
   constexpr int BR = 32 * kNW32;
-  const int nqb = (a.N + BR - 1) / BR;
-  hipLaunchKernelGGL((fwd32_kernel<D, kNW32, kBC32, CAUSAL>), dim3(a.B * a.H * nqb), dim3(kNW32 * 64), 0, a.stream,
-                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.B * a.H, a.N,
-                     a.scale * kLog2e);
+  const int nqb = (a.Nq + BR - 1) / BR;
+  hipLaunchKernelGGL((fwd32_kernel<D, kNW32, kBC32, CAUSAL>), dim3(a.B * a.Hq * nqb), dim3(kNW32 * 64), 0, a.stream,
+                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.B * a.Hq,
+                     a.Hq / a.Hkv, a.Nq, a.Nk, a.scale * kLog2e);
   return hipGetLastError();
 }
 

@@ -17,7 +17,8 @@ struct FwdArgs {
   const void* v;
   void* o;
   float* lse;
-  int B, H, N, d;
+  int B, Hq, Hkv;  // query heads, key/value heads (Hq a multiple of Hkv)
+  int Nq, Nk, d;   // query rows, key rows (causal: Nq <= Nk), head dimension
   float scale;
   bool causal;
   int dtype;
@@ -34,8 +35,9 @@ struct BwdArgs {
   float* dq;
   float* dk;
   float* dv;
-  float* delta;  // workspace: D_i = dO_i . O_i (B*H*N floats), then lse_i*log2(e) (B*H*N)
-  int B, H, N, d;
+  float* delta;  // workspace: D_i = sum_j P_ij dP_ij (B*Hq*Nq floats), then lse_i*log2(e) (B*Hq*Nq)
+  int B, Hq, Hkv;
+  int Nq, Nk, d;
   float scale;
   bool causal;
   int dtype;

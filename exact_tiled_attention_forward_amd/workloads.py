@@ -30,7 +30,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "torch_dtype", "elem_bytes", "fwd_flops", "bwd_flops"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_cross_inputs", "torch_dtype", "elem_bytes", "fwd_flops", "bwd_flops"]
 
 _DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -119,6 +119,19 @@ def make_inputs(B: int, H: int, N: int, d: int, dtype: str, seed_base: int,
     out = {"q": q.to(td).contiguous(), "k": k.to(td).contiguous(), "v": v.to(td).contiguous()}
     if with_do:
         out["do"] = _randn(shape, seed_base + 4).to(td).contiguous()
+    return out
+
+
+def make_cross_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, dtype: str, seed_base: int,
+                      with_do: bool = False):
+    """Like make_inputs for attention with grouped heads and/or different lengths:
+    q (and do) are (B, Hq, Nq, d), k and v are (B, Hkv, Nk, d); same seeds per tensor."""
+    td = torch_dtype(dtype)
+    out = {"q": _randn((B, Hq, Nq, d), seed_base + 1).to(td).contiguous(),
+           "k": _randn((B, Hkv, Nk, d), seed_base + 2).to(td).contiguous(),
+           "v": _randn((B, Hkv, Nk, d), seed_base + 3).to(td).contiguous()}
+    if with_do:
+        out["do"] = _randn((B, Hq, Nq, d), seed_base + 4).to(td).contiguous()
     return out
 
 

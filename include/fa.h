@@ -62,7 +62,8 @@ typedef enum {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,        /* a required pointer is NULL */
-  FA_ERR_SHAPE = -2,       /* B, H or N < 1, or a (B, H, N, d) tensor too large */
+  FA_ERR_SHAPE = -2,       /* a size < 1, Hq not a multiple of Hkv, causal with Nq > Nk,
+                              or a tensor too large for 32-bit offsets within a head */
   FA_ERR_UNSUPPORTED = -3, /* d not in {64, 128}, unknown dtype, or fp32 backward */
   FA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned */
   FA_ERR_WORKSPACE = -5,   /* backward workspace NULL or smaller than required */
@@ -93,8 +94,9 @@ int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * fa_backward_workspace_bytes -- bytes of device workspace fa_backward needs:
- * 8*B*H*N (per query row, D_i = dO_i . O_i and lse_i*log2(e) as floats).  Returns 0 if
- * B, H or N < 1.
+ * 8*B*H*N (per query row, D_i = sum_j P_ij dP_ij and lse_i*log2(e) as floats).  For the
+ * _ex entry points pass the query heads and query rows (Hq, Nq).  Returns 0 if B, H or
+ * N < 1.
  */
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
 
@@ -140,6 +142,45 @@ int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dO
                      float* dk, float* dv, const void* workspace, size_t workspace_bytes,
                      int B, int H, int N, int d, float scale, int causal,
                      fa_dtype_t dtype, hipStream_t stream);
+
+/*
+ * Query and key lengths that differ, and grouped key/value heads
+ * ----------------------------------------------------------------
+ * The pages allow Q and K/V of different lengths (cross-attention, a decode step
+ * against a cached K/V: cf-1.com article, section 3.4) and name grouped-query
+ * attention and causal masks as variants that only skip or mask (i, j) pairs inside
+ * the block loop ("大模型数学速成（17）", section 四).  The _ex entry points take
+ *   q, o, dO, dq    (B, Hq, Nq, d),    lse (B, Hq, Nq) float,
+ *   k, v, dk, dv    (B, Hkv, Nk, d),
+ * with Hq a multiple of Hkv: query head h reads key/value head h / (Hq/Hkv)
+ * (consecutive query heads share one key/value head).  dk and dv of a shared head
+ * are the sums over its query heads (computed in one pass, no atomics).  With
+ * causal != 0 the Nq queries are the last Nq positions of the Nk-long sequence: key j
+ * is visible to query i iff j <= i + (Nk - Nq) (a decode step's query sees the whole
+ * cache); causal with Nq > Nk is rejected with FA_ERR_SHAPE (some rows would see no
+ * key).  Hq % Hkv != 0 is FA_ERR_SHAPE.  The workspace of the backward is
+ * fa_backward_workspace_bytes(B, Hq, Nq, d).  The square entry points above are these
+ * with Hq = Hkv = H and Nq = Nk = N.
+ */
+int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                  fa_dtype_t dtype, hipStream_t stream);
+
+int fa_backward_ex(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                   const float* lse, float* dq, float* dk, float* dv,
+                   void* workspace, size_t workspace_bytes,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   fa_dtype_t dtype, hipStream_t stream);
+
+int fa_backward_dq_ex(const void* q, const void* k, const void* v, const void* dO,
+                      const float* lse, float* dq, void* workspace, size_t workspace_bytes,
+                      int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                      fa_dtype_t dtype, hipStream_t stream);
+
+int fa_backward_dkdv_ex(const void* q, const void* k, const void* v, const void* dO,
+                        float* dk, float* dv, const void* workspace, size_t workspace_bytes,
+                        int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                        fa_dtype_t dtype, hipStream_t stream);
 
 /* fa_status_string -- static, human-readable text for a status code. */
 const char* fa_status_string(int status);

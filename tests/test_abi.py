@@ -125,3 +125,43 @@ def test_python_binding_rejects_host_tensors():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         fa.fa_forward(q, q, q)
+
+
+def fwd_ex(q=P, k=P, v=P, o=P2, lse=P2, B=1, Hq=4, Hkv=2, Nq=16, Nk=16, d=96, scale=0.125, causal=0,
+           dtype=fa.FA_BF16):
+    # d = 96 by default: a call whose other checks pass still fails (FA_ERR_UNSUPPORTED)
+    return fa.library().fa_forward_ex(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, ctypes.c_float(scale), causal, dtype,
+                                      NUL)
+
+
+@needs_lib
+def test_forward_ex_grouping_and_length_errors():
+    assert fwd_ex() == FA_ERR_UNSUPPORTED                      # the grouping and lengths themselves pass
+    assert fwd_ex(Hq=3, Hkv=2) == FA_ERR_SHAPE                 # Hq not a multiple of Hkv
+    assert fwd_ex(Hkv=0) == FA_ERR_SHAPE
+    assert fwd_ex(Nk=0) == FA_ERR_SHAPE
+    assert fwd_ex(Nq=17, Nk=16, causal=1) == FA_ERR_SHAPE      # a causal query row would see no key
+    assert fwd_ex(Nq=17, Nk=16, causal=0) == FA_ERR_UNSUPPORTED
+    assert fwd_ex(Nq=1, Nk=4096, causal=1) == FA_ERR_UNSUPPORTED
+    assert fwd_ex(Nk=1 << 23, d=128, scale=-1.0) == FA_ERR_SHAPE  # a key head of 2^31 fp32 bytes
+    assert fwd_ex(k=NUL) == FA_ERR_NULL
+
+
+@needs_lib
+def test_backward_ex_workspace_is_per_query_row():
+    lib = fa.library()
+    B, Hq, Hkv, Nq, Nk = 2, 8, 2, 48, 80
+    need = lib.fa_backward_workspace_bytes(B, Hq, Nq, 64)
+    assert need == 8 * B * Hq * Nq
+    st = lib.fa_backward_ex(P, P, P, P, P, P2, P2, P2, P2, P2, need - 1, B, Hq, Hkv, Nq, Nk, 64,
+                            ctypes.c_float(0.125), 1, fa.FA_BF16, NUL)
+    assert st == FA_ERR_WORKSPACE
+    st = lib.fa_backward_ex(P, P, P, P, P, P2, P2, P2, P2, P2, need, B, Hq, 3, Nq, Nk, 64,
+                            ctypes.c_float(0.125), 1, fa.FA_BF16, NUL)
+    assert st == FA_ERR_SHAPE
+    st = lib.fa_backward_dq_ex(P, P, P, P, P2, P2, P2, need, B, Hq, Hkv, Nk + 1, Nk, 64,
+                               ctypes.c_float(0.125), 1, fa.FA_BF16, NUL)
+    assert st == FA_ERR_SHAPE
+    st = lib.fa_backward_dkdv_ex(P, P, P, P, P2, P2, P2, need, B, Hq, Hkv, Nq, Nk, 64,
+                                 ctypes.c_float(0.125), 0, fa.FA_F32, NUL)
+    assert st == FA_ERR_UNSUPPORTED
