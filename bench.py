@@ -89,9 +89,10 @@ def algorithmic_bytes(w):
     the logsumexp and writes fp32 dQ plus D and lse*log2(e); bwd_dkdv reads Q, K, V, dO, D
     and lse*log2(e) and writes fp32 dK, dV."""
     s = {"f32": 4, "f16": 2, "bf16": 2}[w.dtype]
-    rows = w.B * w.H * w.N
-    return {"fwd": rows * (4 * w.d * s + 4), "bwd_dq": rows * (4 * w.d * s + 4 + 4 * w.d + 8),
-            "bwd_dkdv": rows * (4 * w.d * s + 8 + 8 * w.d)}
+    qrows, kvrows = w.B * w.H * w.N, w.B * w.Hkv * w.Nk
+    return {"fwd": qrows * (2 * w.d * s + 4) + kvrows * 2 * w.d * s,
+            "bwd_dq": qrows * (2 * w.d * s + 4 + 4 * w.d + 8) + kvrows * 2 * w.d * s,
+            "bwd_dkdv": qrows * (2 * w.d * s + 8) + kvrows * (2 * w.d * s + 8 * w.d)}
 
 
 def _read_counters(path):
@@ -242,20 +243,42 @@ def sweep(names, reps: int, out_path: str):
         q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
         o = torch.empty_like(q)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-        passes = {"fwd": lambda: fa.fa_forward(q, k, v, o, lse, causal=w.causal, stream=stream)}
+        ns = fa.fa_forward_split_count(q, k, w.causal)
+        wsf = None
+        if ns > 1:
+            nbytes = fa.library().fa_forward_split_workspace_bytes(w.B, w.H, w.N, w.d, ns)
+            wsf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        passes = {"fwd": lambda: fa.fa_forward(q, k, v, o, lse, causal=w.causal, stream=stream, split=ns,
+                                               workspace=wsf)}
         if w.backward:
             do = inp["do"].to(dev)
             f32 = torch.float32
-            dq, dk, dv = (torch.empty(q.shape, dtype=f32, device=dev) for _ in range(3))
+            dq = torch.empty(q.shape, dtype=f32, device=dev)
+            dk, dv = (torch.empty(k.shape, dtype=f32, device=dev) for _ in range(2))
             ws = torch.empty(fa.fa_backward_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
             passes["fwd"]()
             passes["bwd"] = lambda: fa.fa_backward(q, k, v, o, do, lse, dq, dk, dv, causal=w.causal, workspace=ws,
                                                  stream=stream)
         s = elem_bytes(w.dtype)
-        unit = 2.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)
-        info = {"fwd": (2 * unit, w.B * w.H * w.N * (4 * w.d * s + 4)),
-                "bwd": (5 * unit, w.B * w.H * w.N * (5 * w.d * s + 3 * w.d * 4 + 8))}
-        small = 4 * w.B * w.H * w.N * w.d * s < (128 << 20)
+        unit = 2.0 * w.B * w.H * w.visible_pairs() * w.d
+        qrows, kvrows = w.B * w.H * w.N, w.B * w.Hkv * w.Nk
+        info = {"fwd": (2 * unit, qrows * (2 * w.d * s + 4) + kvrows * 2 * w.d * s),
+                "bwd": (5 * unit, qrows * (3 * w.d * s + 4 * w.d + 8) + kvrows * (2 * w.d * s + 8 * w.d)),
+                "3step": (2 * unit, qrows * (2 * w.d * s + 4) + kvrows * 2 * w.d * s)}
+        if w.N <= 16:
+            # the plain three-step path for comparison: S = Q K^T, softmax, P V as library calls
+            G = w.H // w.Hkv
+            qg = q.view(w.B, w.Hkv, G * w.N, w.d)
+            kt = k.transpose(-1, -2).contiguous()
+            vc = v.contiguous()
+            sc = 1.0 / math.sqrt(w.d)
+
+            def three_step():
+                sm = torch.matmul(qg, kt).float() * sc
+                p = torch.softmax(sm, dim=-1).to(q.dtype)
+                return torch.matmul(p, vc)
+            passes["3step"] = three_step
+        small = 2 * (qrows + kvrows) * w.d * s < (128 << 20)
         for pname, fn in passes.items():
             for mode in (["warm", "cold"] if small else ["warm"]):
                 for _ in range(10):
@@ -273,8 +296,10 @@ def sweep(names, reps: int, out_path: str):
                 ts.sort()
                 med, mn = ts[len(ts) // 2], ts[0]
                 flops, nbytes = info[pname]
-                rows.append({"workload": name, "shape": f"{w.B}x{w.H}x{w.N}x{w.d}", "dtype": w.dtype,
-                             "causal": w.causal, "pass": pname, "mode": mode, "median_us": med * 1e3,
+                shape = f"{w.B}x{w.H}x{w.N}x{w.d}" if (w.Hkv, w.Nk) == (w.H, w.N) else \
+                    f"{w.B}x{w.H}/{w.Hkv}x{w.N}/{w.Nk}x{w.d}"
+                rows.append({"workload": name, "shape": shape, "dtype": w.dtype,
+                             "causal": w.causal, "pass": pname + (f" (split {ns})" if pname == "fwd" and ns > 1 else ""), "mode": mode, "median_us": med * 1e3,
                              "min_us": mn * 1e3, "tflops": flops / (med * 1e-3) / 1e12,
                              "pct_peak": 100 * flops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                              "gbs": nbytes / (med * 1e-3) / 1e9})
@@ -288,7 +313,9 @@ def sweep(names, reps: int, out_path: str):
         f.write("TFLOP/s use 4BHN^2d (forward) and 10BHN^2d (backward), halved when causal; % of the 2516.6 "
                 "TFLOP/s bf16/fp16 dense MFMA peak (fp32 rows: the same figure, for comparison only); GB/s are "
                 "algorithmic bytes (inputs read once, outputs written once) over the median time.  cold = a "
-                "512 MB fill between launches.\n\n")
+                "512 MB fill between launches.  Shapes with a slash are query/key-value heads and query/key rows; "
+                "3step is the plain S = QK^T, softmax, PV path as three library calls (torch matmul and softmax), "
+                "timed for comparison on decode shapes.\n\n")
         f.write("| workload | B x H x N x d | dtype | causal | pass | mode | median (us) | min (us) | TFLOP/s "
                 "| % peak | GB/s |\n|---|---|---|---|---|---|---|---|---|---|---|\n")
         for r in rows:
@@ -302,7 +329,7 @@ def kernel_flops(w):
     """Credited (algorithmic) flops of each kernel per launch.  The forward kernel owns
     S = QK^T and O = PV; of the backward's five products the dK/dV kernel owns S, dP,
     dV and dK, the dQ kernel owns dQ."""
-    unit = 2.0 * w.B * w.H * w.N * w.N * w.d * (0.5 if w.causal else 1.0)  # one N x N x d product
+    unit = 2.0 * w.B * w.H * w.visible_pairs() * w.d  # one N x N x d product (half of it when causal)
     return {"fwd": 2 * unit, "bwd_dq": 1 * unit, "bwd_dkdv": 4 * unit}
 
 
@@ -380,7 +407,8 @@ def main():
         sys.exit(2)
 
     if args.sweep:
-        names = ["single_head_f32", "prefill_bf16", "gpt2_medium_train", "long_f16", "long_bf16", "large_head_causal"]
+        names = ["single_head_f32", "prefill_bf16", "gpt2_medium_train", "long_f16", "long_bf16", "large_head_causal",
+                 "gqa_causal_train", "decode_gqa"]
         log("wrote", sweep(names, args.sweep_reps, os.path.join(PROFILES, "timing_all_workloads.md")))
         return
 

@@ -22,7 +22,7 @@ import os
 
 import torch  # the HIP runtime torch loads is the one libfa.so binds to (same soname)
 
-__all__ = ["fa_forward", "fa_backward", "fa_backward_dq", "fa_backward_dkdv", "fa_backward_workspace_bytes",
+__all__ = ["fa_forward", "fa_forward_split_count", "fa_backward", "fa_backward_dq", "fa_backward_dkdv", "fa_backward_workspace_bytes",
            "library", "FAError", "FA_F32", "FA_F16", "FA_BF16", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -68,6 +68,12 @@ def library() -> ctypes.CDLL:
     lib.fa_backward_dq_ex.restype = i
     lib.fa_backward_dkdv_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, i, i, vp]
     lib.fa_backward_dkdv_ex.restype = i
+    lib.fa_forward_split_count.argtypes = [i, i, i, i, i, i, i, i]
+    lib.fa_forward_split_count.restype = i
+    lib.fa_forward_split_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_forward_split_workspace_bytes.restype = sz
+    lib.fa_forward_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, i, vp]
+    lib.fa_forward_split.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -111,12 +117,24 @@ def _shapes(q, k):
     return B, Hq, Hkv, Nq, Nk, d
 
 
-def fa_forward(q, k, v, o=None, lse=None, *, scale=None, causal=False, stream=None):
+def fa_forward_split_count(q, k, causal=False):
+    """The key-range split count the library suggests for these shapes (1: no split)."""
+    B, Hq, Hkv, Nq, Nk, d = _shapes(q, k)
+    return int(library().fa_forward_split_count(B, Hq, Hkv, Nq, Nk, d, int(bool(causal)),
+                                                _DTYPE_CODE.get(q.dtype, -1)))
+
+
+def fa_forward(q, k, v, o=None, lse=None, *, scale=None, causal=False, stream=None, split=None, workspace=None):
     """O, lse = attention(q, k, v).
 
     q (B, Hq, Nq, d); k, v (B, Hkv, Nk, d) with Hq a multiple of Hkv (query head h
     reads key/value head h // (Hq // Hkv)); o like q; lse (B, Hq, Nq) float32.  With
     causal=True the queries are the last Nq positions of the Nk keys.
+
+    ``split``: None lets the library choose (fa_forward_split_count: more than one only
+    when the grid is too small to fill the GPU, e.g. a decode step), 1 forces one pass
+    over the keys, n > 1 splits each query block's key range in up to n chunks merged
+    afterwards.  ``workspace`` (uint8, optional) holds the split partials.
     """
     lib = library()
     B, Hq, Hkv, Nq, Nk, d = _shapes(q, k)
@@ -133,6 +151,16 @@ def fa_forward(q, k, v, o=None, lse=None, *, scale=None, causal=False, stream=No
     po = _gpu_tensor("o", o, dt, q.shape)
     pl = _gpu_tensor("lse", lse, torch.float32, (B, Hq, Nq))
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    ns = fa_forward_split_count(q, k, causal) if split is None else int(split)
+    if ns > 1:
+        need = int(lib.fa_forward_split_workspace_bytes(B, Hq, Nq, d, ns))
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        pw = _gpu_tensor("workspace", workspace)
+        _check(lib.fa_forward_split(pq, pk, pv, po, pl, B, Hq, Hkv, Nq, Nk, d, ctypes.c_float(sc),
+                                    int(bool(causal)), ns, pw, workspace.numel() * workspace.element_size(),
+                                    _DTYPE_CODE[dt], _stream(stream, q.device)))
+        return o, lse
     _check(lib.fa_forward_ex(pq, pk, pv, po, pl, B, Hq, Hkv, Nq, Nk, d, ctypes.c_float(sc), int(bool(causal)),
                              _DTYPE_CODE[dt], _stream(stream, q.device)))
     return o, lse

@@ -9,7 +9,8 @@
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0
+constexpr int kVersion = 300;  // 0.3.0
+constexpr int kMaxSplits = 1024;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -59,6 +60,40 @@ int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* l
 
   fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal != 0, (int)dtype, stream};
   (void)hipGetLastError();  // clear a pending error so the check below is about this launch
+  if (fa::launch_forward(a) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+int fa_forward_split_count(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, fa_dtype_t dtype) {
+  if (check_shape(B, Hq, Hkv, Nq, Nk, d, (int)dtype, causal) != FA_OK) return 1;
+  return fa::fwd_suggest_splits(B, Hq, Hkv, Nq, Nk, d, causal != 0, (int)dtype);
+}
+
+size_t fa_forward_split_workspace_bytes(int B, int Hq, int Nq, int d, int nsplit) {
+  if (B < 1 || Hq < 1 || Nq < 1 || nsplit < 2 || nsplit > kMaxSplits) return 0;
+  return fa::fwd_split_bytes(B, Hq, Nq, d, nsplit);
+}
+
+int fa_forward_split(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
+                     int Nk, int d, float scale, int causal, int nsplit, void* workspace, size_t workspace_bytes,
+                     fa_dtype_t dtype, hipStream_t stream) {
+  if (nsplit == 1) return fa_forward_ex(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, stream);
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (nsplit < 1 || nsplit > kMaxSplits) return FA_ERR_SHAPE;
+  int st = check_shape(B, Hq, Hkv, Nq, Nk, d, (int)dtype, causal);
+  if (st != FA_OK) return st;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  // grid: every (key/value head, query block) times the splits
+  if ((int64_t)B * Hq * ((Nq + 31) / 32 + 1) * nsplit >= (int64_t)1 << 31) return FA_ERR_SHAPE;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse)) return FA_ERR_ALIGN;
+  if (!workspace || workspace_bytes < fa::fwd_split_bytes(B, Hq, Nq, d, nsplit)) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal != 0, (int)dtype, stream};
+  a.nsplit = nsplit;
+  a.part = (float*)workspace;
+  (void)hipGetLastError();
   if (fa::launch_forward(a) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
 }

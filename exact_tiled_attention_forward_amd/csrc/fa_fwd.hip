@@ -47,10 +47,96 @@ namespace fa {
 // ----------------------------------------------------------------------------------
 constexpr float kRescaleSlack = 8.0f;
 
-template <class T, int D, int NW, int BC, int WPE, bool CAUSAL>
+// Rows of the 16-bit kernel: the G*Nq query rows of one key/value head's group, packed.
+// The group's query heads are consecutive, so its rows are contiguous in Q and O, and
+// packed row r is position r % Nq of query head (group's first head + r / Nq).  Packing
+// lets one workgroup serve a whole group when G*Nq is small (a decode step), so the
+// group's K/V tiles are read once.
+//
+// Positions of the packed rows [r0, r1] (r0 <= r1): contiguous inside one head, else
+// every position (a conservative range for the causal skip and mask decisions).
+__host__ __device__ inline void pos_range(int r0, int r1, int Nq, int& pmin, int& pmax) {
+  if (r0 / Nq == r1 / Nq) {
+    pmin = r0 % Nq;
+    pmax = r1 % Nq;
+  } else {
+    pmin = 0;
+    pmax = Nq - 1;
+  }
+}
+
+// Key tiles a query block of packed rows [q0, q0 + BR) needs: all of them, or with causal
+// masking those up to the last position of the block plus Nk - Nq.  The split epilogue's
+// merge uses the same count to know which partial results exist.
+template <int BR, int BC, bool CAUSAL>
+__host__ __device__ inline int block_key_tiles(int q0, int R, int Nq, int Nk) {
+  const int nkt_all = (Nk + BC - 1) / BC;
+  if (!CAUSAL) return nkt_all;
+  int pmin, pmax;
+  const int r1 = q0 + BR - 1 < R - 1 ? q0 + BR - 1 : R - 1;
+  pos_range(q0, r1, Nq, pmin, pmax);
+  const int kt = (pmax + Nk - Nq) / BC + 1;
+  return kt < nkt_all ? kt : nkt_all;
+}
+
+struct Fwd16Params {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  uint16_t* O;
+  float* LSE;
+  int BHkv, G, Nq, Nk;  // key/value heads (B*Hkv), query heads per group, lengths
+  float c;              // scale * log2(e)
+  int ct;               // key tiles per split (>= every block's tile count: no split)
+  int nsplit;           // splits the partial buffer holds
+  float* part;          // split partials: o [s][row][D], then m, l, lr [s][row]
+};
+
+// Merge of the split partials of one packed row with the (m, l) rule of the tiled
+// method ("FlashAttention：IO 感知…", 基准/方法设计): with M = max_s m_s and
+// a_s = 2^(m_s - M), O = sum_s a_s o_s / sum_s a_s lr_s and lse = M + log2(sum_s a_s l_s)
+// (base 2, converted to natural log).  One wave per row, D/64 elements per lane.
+template <class T, int D, int NW, int BR, int BC, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void fwd_merge_kernel(const Fwd16Params P) {
+  const int R = P.G * P.Nq;
+  const size_t nrows = (size_t)P.BHkv * R;
+  const size_t g = (size_t)blockIdx.x * NW + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (g >= nrows) return;
+  const int r = (int)(g % R);
+  const int ktiles = block_key_tiles<BR, BC, CAUSAL>((r / BR) * BR, R, P.Nq, P.Nk);
+  const int ns = (ktiles + P.ct - 1) / P.ct;  // splits that wrote a partial for this row
+  const float* pm = P.part + (size_t)P.nsplit * nrows * D;
+  const float* pl = pm + (size_t)P.nsplit * nrows;
+  const float* plr = pl + (size_t)P.nsplit * nrows;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[s * nrows + g]);  // finite: split 0 holds key 0
+  constexpr int E = D / 64;
+  float acc[E] = {};
+  float lt = 0.f, lr = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float ms = pm[s * nrows + g];
+    const float a = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
+    lt += a * pl[s * nrows + g];
+    lr += a * plr[s * nrows + g];
+    const float* po = P.part + (s * nrows + g) * D + E * lane;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] += a * po[e];
+  }
+  const float inv = 1.0f / lr;
+  uint16_t* orow = P.O + g * D + E * lane;
+  if constexpr (E == 2) {
+    *(uint32_t*)orow = T::pack(acc[0] * inv, acc[1] * inv);
+  } else {
+    const uint32_t w = T::pack(acc[0] * inv, 0.f);
+    *orow = (uint16_t)(w & 0xffffu);
+  }
+  if (lane == 0) P.LSE[g] = (M + log2f(lt)) * kLn2;
+}
+
+template <class T, int D, int NW, int BC, int WPE, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void fwd16_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int G, int Nq, int Nk, float c) {
+    const Fwd16Params P) {
   constexpr int BR = 32 * NW;
   constexpr int NT = NW * 64;
   constexpr int TB = BC * D * 2;  // bytes of one K or V tile
@@ -61,29 +147,37 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TB];  // K0 K1 V0 V1
   FA_LDS uint8_t* lds = (FA_LDS uint8_t*)(smem);
 
+  const int Nq = P.Nq, Nk = P.Nk, R = P.G * P.Nq;
+  const float c = P.c;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, c32 = lane & 31;
-  const int nqb = (Nq + BR - 1) / BR;
-  const int bh = blockIdx.x % BH;
-  int qb = blockIdx.x / BH;
+  const int nqb = (R + BR - 1) / BR;
+  const int bkv = blockIdx.x % P.BHkv;
+  const int t = blockIdx.x / P.BHkv;
+  int qb = t % nqb;
+  const int split = t / nqb;
   if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
   const int q0 = qb * BR;
   const int qw0 = q0 + 32 * wave;
-  const int qrow = qw0 + c32;
+  const int qrow = qw0 + c32;          // packed row of this lane
+  const int pos = qrow % Nq;           // its position among the Nq queries
+  const int off = Nk - Nq;             // causal: position i sees keys j <= i + off
+  const bool wave_rows = qw0 < R;      // the wave holds at least one real row
+  int wpmin = 0, wpmax = -1;
+  if (wave_rows) pos_range(qw0, min(qw0 + 31, R - 1), Nq, wpmin, wpmax);
 
-  // query head bh reads key/value head bh / G; causal: query row i sits at position
-  // i + off of the key sequence and sees keys j <= i + off
-  const size_t head = (size_t)bh * Nq * D;
-  const size_t kvhead = (size_t)(bh / G) * Nk * D;
-  const int off = Nk - Nq;
-  const auto rq = make_rsrc(Q + head, (uint32_t)Nq * D * 2);
-  const auto rk = make_rsrc(K + kvhead, (uint32_t)Nk * D * 2);
-  const auto rv = make_rsrc(V + kvhead, (uint32_t)Nk * D * 2);
+  const int ktiles = block_key_tiles<BR, BC, CAUSAL>(q0, R, Nq, Nk);
+  const int j0 = SPLIT ? split * P.ct : 0;
+  const int j1 = SPLIT ? min(j0 + P.ct, ktiles) : ktiles;
+  if (j0 >= j1) return;  // an empty split: the merge does not read it
 
-  const int nkt_all = (Nk + BC - 1) / BC;
-  const int nkt = CAUSAL ? min(nkt_all, (q0 + BR - 1 + off) / BC + 1) : nkt_all;
+  const size_t head = (size_t)bkv * R * D;   // the group's first query row
+  const size_t kvhead = (size_t)bkv * Nk * D;
+  const auto rq = make_rsrc(P.Q + head, (uint32_t)R * D * 2);
+  const auto rk = make_rsrc(P.K + kvhead, (uint32_t)Nk * D * 2);
+  const auto rv = make_rsrc(P.V + kvhead, (uint32_t)Nk * D * 2);
 
-  tile_load_async<D, BC, NT>(lds, rk, 0, tid);
-  tile_load_async<D, BC, NT>(lds + 2 * TB, rv, 0, tid);
+  tile_load_async<D, BC, NT>(lds, rk, j0 * BC, tid);
+  tile_load_async<D, BC, NT>(lds + 2 * TB, rv, j0 * BC, tid);
 
   u32x4 qf[DS];
 #pragma unroll
@@ -91,22 +185,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 
   // base-2 exponent reference m (of s*c); this half's running sums: l of the fp32
   // probabilities (for the logsumexp) and lr of the same probabilities rounded to 16 bits
-  // (for O)
+  // (for O).  m stays -inf while every key seen so far is masked for the row (only
+  // possible in a split that starts past a row's last visible key).
   float m = -INFINITY, l = 0.f, lr = 0.f;
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
 
-  for (int j = 0; j < nkt; ++j) {
+  for (int j = j0; j < j1; ++j) {
     wait_vmem();
     __syncthreads();
-    const int cur = j & 1;
-    if (j + 1 < nkt) {
+    const int cur = (j - j0) & 1;
+    if (j + 1 < j1) {
       tile_load_async<D, BC, NT>(lds + (cur ^ 1) * TB, rk, (j + 1) * BC, tid);
       tile_load_async<D, BC, NT>(lds + (2 + (cur ^ 1)) * TB, rv, (j + 1) * BC, tid);
     }
     const int k0 = j * BC;
-    if (CAUSAL && k0 > qw0 + 31 + off) continue;  // every key of the tile is in this wave's future
+    if (!wave_rows || (CAUSAL && k0 > wpmax + off)) continue;  // no row of the wave sees the tile
     const FA_LDS uint8_t* kt = lds + cur * TB;
     const FA_LDS uint8_t* vt = lds + (2 + cur) * TB;
 
@@ -119,14 +214,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       for (int st = 0; st < DS; ++st) s[kb] = T::mfma(lds_row16<D>(kt, 32 * kb + c32, 2 * st + half), qf[st], s[kb]);
     }
 
-    // masks: keys past the end, and (causal) keys after the query
-    if ((k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw0 + off)) {
+    // masks: keys past the end, and (causal) keys after the query's position
+    if ((k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > wpmin + off)) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + 32 * kb + acc_row(i, half);
-          s[kb][i] = (key >= Nk || (CAUSAL && key > qrow + off)) ? -INFINITY : s[kb][i];
+          s[kb][i] = (key >= Nk || (CAUSAL && key > pos + off)) ? -INFINITY : s[kb][i];
         }
     }
 
@@ -138,25 +233,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       for (int i = 0; i < 16; i += 2) mx = max_nan(max_nan(mx, s[kb][i]), s[kb][i + 1]);
     mx = max_halves(mx) * c;
     if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m, mx);  // finite: the first tile always holds key 0
-      const float alpha = fast_exp2(m - m_new);
+      const float m_new = fmaxf(m, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m - m_new);  // o, l are 0 while m = -inf
       l *= alpha;
       lr *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
       m = m_new;
     }
+    const float mu = (m == -INFINITY) ? 0.f : m;  // every score of such a row is -inf: p = 0
     float rs = 0.f, rsr = 0.f;
     uint32_t pk[KB][8];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float p0 = fast_exp2(fmaf(s[kb][2 * t], c, -m));
-        const float p1 = fast_exp2(fmaf(s[kb][2 * t + 1], c, -m));
+      for (int t2 = 0; t2 < 8; ++t2) {
+        const float p0 = fast_exp2(fmaf(s[kb][2 * t2], c, -mu));
+        const float p1 = fast_exp2(fmaf(s[kb][2 * t2 + 1], c, -mu));
         rs += p0 + p1;
-        pk[kb][t] = T::pack(p0, p1);
-        rsr = T::sum2(pk[kb][t], rsr);
+        pk[kb][t2] = T::pack(p0, p1);
+        rsr = T::sum2(pk[kb][t2], rsr);
       }
     l += rs;
     lr += rsr;
@@ -171,25 +267,47 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     }
   }
 
-  // epilogue: one division per row, 16-bit O, natural-log LSE.  O divides by the sum of
-  // the rounded probabilities the P V product used, which makes it an exact weighted
-  // average of V rows; the logsumexp uses the fp32 sum.
   const float lt = sum_halves(l);
-  const float inv = 1.0f / sum_halves(lr);
-  if (qrow < Nq) {
-    uint16_t* orow = O + head + (size_t)qrow * D;
+  const float ltr = sum_halves(lr);
+  if (qrow >= R) return;
+  if (SPLIT) {
+    // partial result of this split: unnormalised o (fp32), the exponent reference m and
+    // both sums, merged by fwd_merge_kernel with the (m, l) rule
+    const size_t nrows = (size_t)P.BHkv * R;
+    const size_t row = (size_t)split * nrows + (size_t)bkv * R + qrow;
+    float* prow = P.part + row * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * db + 8 * g + 4 * half;
-        u32x2 w;
-        w.x = T::pack(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
-        w.y = T::pack(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-        *(u32x2*)(orow + d) = w;
+        *(f32x4*)(prow + d) = (f32x4){o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
       }
-    if (half == 0) LSE[(size_t)bh * Nq + qrow] = (m + log2f(lt)) * kLn2;
+    if (half == 0) {
+      float* pm = P.part + (size_t)P.nsplit * nrows * D;  // m [s][row], l, lr after it
+      const size_t i = (size_t)split * nrows + (size_t)bkv * R + qrow;
+      pm[i] = m;
+      pm[(size_t)P.nsplit * nrows + i] = lt;
+      pm[(size_t)2 * P.nsplit * nrows + i] = ltr;
+    }
+    return;
   }
+  // epilogue: one division per row, 16-bit O, natural-log LSE.  O divides by the sum of
+  // the rounded probabilities the P V product used, which makes it an exact weighted
+  // average of V rows; the logsumexp uses the fp32 sum.
+  const float inv = 1.0f / ltr;
+  uint16_t* orow = P.O + head + (size_t)qrow * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * db + 8 * g + 4 * half;
+      u32x2 w;
+      w.x = T::pack(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+      w.y = T::pack(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+      *(u32x2*)(orow + d) = w;
+    }
+  if (half == 0) P.LSE[(size_t)bkv * R + qrow] = (m + log2f(lt)) * kLn2;
 }
 
 // ----------------------------------------------------------------------------------
@@ -347,10 +465,35 @@ template <class T, int D, bool CAUSAL>
 hipError_t go16(const FwdArgs& a) {
   using S = Fwd16Shape<D>;
   constexpr int BR = 32 * S::NW;
-  const int nqb = (a.Nq + BR - 1) / BR;
-  hipLaunchKernelGGL((fwd16_kernel<T, D, S::NW, S::BC, S::WPE, CAUSAL>), dim3(a.B * a.Hq * nqb), dim3(S::NW * 64), 0,
-                     a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                     a.B * a.Hq, a.Hq / a.Hkv, a.Nq, a.Nk, a.scale * kLog2e);
+  const int R = (a.Hq / a.Hkv) * a.Nq;
+  const int nqb = (R + BR - 1) / BR;
+  const int BHkv = a.B * a.Hkv;
+  Fwd16Params p{(const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
+                BHkv, a.Hq / a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, 0, 1, nullptr};
+  if (a.nsplit <= 1) {
+    p.ct = (a.Nk + S::BC - 1) / S::BC;
+    hipLaunchKernelGGL((fwd16_kernel<T, D, S::NW, S::BC, S::WPE, CAUSAL, false>), dim3(BHkv * nqb),
+                       dim3(S::NW * 64), 0, a.stream, p);
+    return hipGetLastError();
+  }
+  // split the key range of the longest query block into nsplit chunks of ct tiles
+  int max_tiles = 0;
+  for (int qb = 0; qb < nqb; ++qb) {
+    const int kt = block_key_tiles<BR, S::BC, CAUSAL>(qb * BR, R, a.Nq, a.Nk);
+    max_tiles = kt > max_tiles ? kt : max_tiles;
+  }
+  p.ct = (max_tiles + a.nsplit - 1) / a.nsplit;
+  const int ns = (max_tiles + p.ct - 1) / p.ct;
+  p.nsplit = a.nsplit;
+  p.part = a.part;
+  hipLaunchKernelGGL((fwd16_kernel<T, D, S::NW, S::BC, S::WPE, CAUSAL, true>), dim3(BHkv * nqb * ns),
+                     dim3(S::NW * 64), 0, a.stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int NWM = 4;
+  const long nrows = (long)BHkv * R;
+  hipLaunchKernelGGL((fwd_merge_kernel<T, D, NWM, BR, S::BC, CAUSAL>), dim3((nrows + NWM - 1) / NWM), dim3(NWM * 64),
+                     0, a.stream, p);
   return hipGetLastError();
 }
 
@@ -374,6 +517,40 @@ hipError_t by_dtype(const FwdArgs& a) {
   return hipErrorInvalidValue;
 }
 }  // namespace
+
+namespace {
+template <int D, bool CAUSAL>
+int max_block_tiles(int R, int Nq, int Nk) {
+  using S = Fwd16Shape<D>;
+  constexpr int BR = 32 * S::NW;
+  const int nqb = (R + BR - 1) / BR;
+  int mt = 0;
+  for (int qb = 0; qb < nqb; ++qb) {
+    const int kt = block_key_tiles<BR, S::BC, CAUSAL>(qb * BR, R, Nq, Nk);
+    mt = kt > mt ? kt : mt;
+  }
+  return mt;
+}
+}  // namespace
+
+int fwd_suggest_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, bool causal, int dtype) {
+  if (dtype == kDtypeF32) return 1;
+  const int NW = d == 64 ? Fwd16Shape<64>::NW : Fwd16Shape<128>::NW;
+  const int BR = 32 * NW;
+  const long R = (long)(Hq / Hkv) * Nq;
+  const long wg = (long)B * Hkv * ((R + BR - 1) / BR);
+  constexpr long kTarget = 512;  // two workgroups for each of the 256 CUs
+  if (wg >= kTarget) return 1;
+  const int mt = d == 64 ? (causal ? max_block_tiles<64, true>((int)R, Nq, Nk) : max_block_tiles<64, false>((int)R, Nq, Nk))
+                         : (causal ? max_block_tiles<128, true>((int)R, Nq, Nk)
+                                   : max_block_tiles<128, false>((int)R, Nq, Nk));
+  long want = (kTarget + wg - 1) / wg;
+  if (want > mt) want = mt;
+  if (want > 64) want = 64;
+  if (want < 2) return 1;
+  const int ct = (int)((mt + want - 1) / want);
+  return (mt + ct - 1) / ct;
+}
 
 hipError_t launch_forward(const FwdArgs& a) {
   return a.d == 64 ? by_dtype<64>(a) : by_dtype<128>(a);

@@ -23,7 +23,19 @@ struct FwdArgs {
   bool causal;
   int dtype;
   hipStream_t stream;
+  int nsplit = 1;          // > 1: split each query block's key range (16-bit inputs only)
+  float* part = nullptr;   // workspace for the split partials (fwd_split_bytes)
 };
+
+// Bytes of the split partials: nsplit x (B*Hq*Nq rows) x (d + 3) floats.
+inline size_t fwd_split_bytes(int B, int Hq, int Nq, int d, int nsplit) {
+  return (size_t)nsplit * B * Hq * Nq * (d + 3) * sizeof(float);
+}
+
+// Split count the library suggests: none when the unsplit grid already gives every CU
+// two workgroups, else enough chunks of the longest query block's key range to reach
+// about 512 workgroups.
+int fwd_suggest_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, bool causal, int dtype);
 
 struct BwdArgs {
   const void* q;

@@ -16,6 +16,10 @@ Workloads (B, H, N, d, storage dtype, causal):
   are scaled by 8 (exact in bf16) to stress the running-max rescaling.
 * ``smoke_2x4x512``        2, 4,   512,  64, bf16, no   -- the consistency smoke test
   shape and seed 0 from the cf-1.com article, section 3.3.
+* ``gqa_causal_train``     1, 32 query / 8 key-value heads, 8192, 128, bf16, yes -- forward +
+  backward with grouped heads.
+* ``decode_gqa``           8, 32 query / 8 key-value heads, 1 query row against 8192 cached
+  keys, 128, bf16, causal (the query is the newest position) -- forward only.
 
 Recipe: each tensor is drawn i.i.d. N(0, 1) in fp32 on the CPU with
 ``torch.Generator().manual_seed(seed)`` and cast (round-to-nearest-even) to the storage
@@ -57,10 +61,30 @@ class Workload:
     outlier_frac: float = 0.0
     outlier_scale: float = 1.0
     note: str = field(default="", compare=False)
+    Hkv_: int = 0  # key/value heads (0: H, one per query head)
+    Nk_: int = 0   # key rows (0: N)
 
     @property
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.d)
+
+    @property
+    def Hkv(self) -> int:
+        return self.Hkv_ or self.H
+
+    @property
+    def Nk(self) -> int:
+        return self.Nk_ or self.N
+
+    def visible_pairs(self) -> float:
+        """(query, key) pairs per head that the work convention counts: N^2/2 for square
+        causal attention (the usual halving), the exact count when N_q < N_k."""
+        nq, nk = self.N, self.Nk
+        if not self.causal:
+            return float(nq * nk)
+        if nq == nk:
+            return nq * nk / 2.0
+        return float(nq * nk - nq * (nq - 1) // 2)
 
     def shape(self):
         return (self.B, self.H, self.N, self.d)
@@ -76,6 +100,8 @@ WORKLOADS = {
         Workload("long_bf16", 1, 16, 16384, 64, "bf16", False, False, 42000),
         Workload("large_head_causal", 2, 16, 8192, 128, "bf16", True, True, 5000, 0.05, 8.0),
         Workload("smoke_2x4x512", 2, 4, 512, 64, "bf16", False, False, 0),
+        Workload("gqa_causal_train", 1, 32, 8192, 128, "bf16", True, True, 6000, Hkv_=8),
+        Workload("decode_gqa", 8, 32, 1, 128, "bf16", True, False, 7000, Hkv_=8, Nk_=8192),
     ]
 }
 
@@ -137,8 +163,10 @@ def make_cross_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, dtype
 
 def workload_inputs(w: Workload, with_do: bool | None = None):
     """Inputs of a named workload at its full size."""
-    return make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed_base, w.outlier_frac, w.outlier_scale,
-                       with_do=w.backward if with_do is None else with_do)
+    with_do = w.backward if with_do is None else with_do
+    if w.Hkv != w.H or w.Nk != w.N:
+        return make_cross_inputs(w.B, w.H, w.Hkv, w.N, w.Nk, w.d, w.dtype, w.seed_base, with_do=with_do)
+    return make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed_base, w.outlier_frac, w.outlier_scale, with_do=with_do)
 
 
 def fwd_flops(B: int, H: int, N: int, d: int, causal: bool) -> float:

@@ -182,6 +182,38 @@ int fa_backward_dkdv_ex(const void* q, const void* k, const void* v, const void*
                         int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                         fa_dtype_t dtype, hipStream_t stream);
 
+/*
+ * Split key range (decode steps and other small grids)
+ * ----------------------------------------------------
+ * When B*Hkv*ceil(G*Nq / rows-per-workgroup) workgroups cannot fill the 256 CUs (a
+ * decode step has one query row per head; a short batch of long causal rows leaves the
+ * longest row to one workgroup), fa_forward_split cuts the key range of every query
+ * block into up to `nsplit` chunks, computes each chunk's partial result (unnormalised
+ * o, running max m and sums l in the tiled recurrence) in its own workgroup, and merges
+ * them with the pages' (m, l) merge rule ("FlashAttention：IO 感知…", 基准/方法设计:
+ * m = max(m1, m2), l = e^(m1-m) l1 + e^(m2-m) l2, and the same factors on o), which is
+ * exact up to rounding order.  The rows of one key/value head's group are processed
+ * together, so the group's K and V are read once per chunk.
+ *   fa_forward_split_count    the split count the library suggests for these arguments
+ *                             (1: the unsplit grid already gives each CU two workgroups).
+ *   fa_forward_split_workspace_bytes
+ *                             nsplit * B*Hq*Nq * (d + 3) * 4 bytes for nsplit >= 2 (0 for
+ *                             nsplit < 2 or > 1024).
+ *   fa_forward_split          as fa_forward_ex plus nsplit in [1, 1024] and a 16-byte
+ *                             aligned device workspace of at least that size (contents on
+ *                             entry ignored; NULL allowed when nsplit == 1, which is exactly
+ *                             fa_forward_ex).  16-bit inputs only for nsplit > 1
+ *                             (FA_ERR_UNSUPPORTED for fp32).  Two kernels on `stream`.
+ */
+int fa_forward_split_count(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, fa_dtype_t dtype);
+
+size_t fa_forward_split_workspace_bytes(int B, int Hq, int Nq, int d, int nsplit);
+
+int fa_forward_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                     int nsplit, void* workspace, size_t workspace_bytes,
+                     fa_dtype_t dtype, hipStream_t stream);
+
 /* fa_status_string -- static, human-readable text for a status code. */
 const char* fa_status_string(int status);
 

@@ -165,3 +165,24 @@ def test_backward_ex_workspace_is_per_query_row():
     st = lib.fa_backward_dkdv_ex(P, P, P, P, P2, P2, P2, need, B, Hq, Hkv, Nq, Nk, 64,
                                  ctypes.c_float(0.125), 0, fa.FA_F32, NUL)
     assert st == FA_ERR_UNSUPPORTED
+
+
+@needs_lib
+def test_split_entry_points_validate_before_launch():
+    lib = fa.library()
+    assert lib.fa_forward_split_workspace_bytes(2, 8, 1, 128, 4) == 4 * 2 * 8 * 1 * (128 + 3) * 4
+    assert lib.fa_forward_split_workspace_bytes(2, 8, 1, 128, 1) == 0
+    assert lib.fa_forward_split_workspace_bytes(2, 8, 1, 128, 1025) == 0
+    # a decode step (one query row per head) is split; a large grid is not
+    assert lib.fa_forward_split_count(8, 32, 8, 1, 8192, 128, 1, fa.FA_BF16) > 1
+    assert lib.fa_forward_split_count(2, 16, 16, 8192, 8192, 128, 1, fa.FA_BF16) == 1
+    assert lib.fa_forward_split_count(1, 1, 1, 256, 256, 64, 0, fa.FA_F32) == 1
+    need = lib.fa_forward_split_workspace_bytes(1, 4, 1, 128, 4)
+    args = (P, P, P, P2, P2, 1, 4, 2, 1, 512, 128, ctypes.c_float(0.125), 1)
+    assert lib.fa_forward_split(*args, 4, P2, need - 1, fa.FA_BF16, NUL) == FA_ERR_WORKSPACE
+    assert lib.fa_forward_split(*args, 4, NUL, need, fa.FA_BF16, NUL) == FA_ERR_WORKSPACE
+    assert lib.fa_forward_split(*args, 4, MIS, need, fa.FA_BF16, NUL) == FA_ERR_ALIGN
+    assert lib.fa_forward_split(*args, 0, P2, need, fa.FA_BF16, NUL) == FA_ERR_SHAPE
+    assert lib.fa_forward_split(*args, 4, P2, need, fa.FA_F32, NUL) == FA_ERR_UNSUPPORTED
+    bad = (P, P, P, P2, P2, 1, 4, 3, 1, 512, 128, ctypes.c_float(0.125), 1)
+    assert lib.fa_forward_split(*bad, 4, P2, need, fa.FA_BF16, NUL) == FA_ERR_SHAPE
