@@ -24,6 +24,13 @@ Readings where the pages are silent (each also listed in the design doc):
   the tiling): H_q query heads share H_kv key/value heads, H_q = G * H_kv; query
   head h reads key/value head h // G (consecutive query heads form a group).  In
   the backward, the gradient of a shared K or V head is the sum over its group.
+* block-sparse masks ([FA-nips] 方法细节 and its LRA results: block-sparse
+  FlashAttention skips whole zero blocks of a given block mask): a mask of
+  (heads, ceil(N_q/128), ceil(N_k/128)) bytes, shared by the batch, one layer or
+  one per query head; block (i//128, j//128) == 0 hides key j from query i (on top
+  of the causal mask).  A query row with no visible key has P = 0, O = 0 and
+  LSE = -inf (and zero gradients), the usual reading of an empty softmax in
+  masked attention.
 * LSE_i = m_i + ln(l_i): the natural-log logsumexp of the scaled, masked row; the
   pages save (m, l) per row ([FA-ch] FlashAttention section on recomputation,
   [FA-nips] 方法细节), and m + ln l carries the same information.
@@ -41,7 +48,9 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
+    "BLOCK",
     "causal_mask",
+    "expand_block_mask",
     "kv_head",
     "scores",
     "softmax_rows",
@@ -75,14 +84,31 @@ def kv_head(h: int, h_q: int, h_kv: int) -> int:
     return h // (h_q // h_kv)
 
 
-def scores(q: np.ndarray, k: np.ndarray, scale: float, causal: bool) -> np.ndarray:
+BLOCK = 128  # rows and columns of one block of a block-sparse mask
+
+
+def expand_block_mask(block_mask_head, n_q: int, n_k: int, block: int = BLOCK) -> np.ndarray:
+    """Boolean (n_q, n_k) array, True where key j is hidden from query i because block
+    (i // block, j // block) of the (ceil(n_q/block), ceil(n_k/block)) block mask is 0."""
+    bm = np.asarray(block_mask_head)
+    nb_q, nb_k = -(-n_q // block), -(-n_k // block)
+    if bm.shape != (nb_q, nb_k):
+        raise ValueError(f"block mask must be ({nb_q}, {nb_k}) for n_q={n_q}, n_k={n_k}")
+    keep = np.repeat(np.repeat(bm != 0, block, axis=0), block, axis=1)[:n_q, :n_k]
+    return ~keep
+
+
+def scores(q: np.ndarray, k: np.ndarray, scale: float, causal: bool, hidden=None) -> np.ndarray:
     """S = scale * Q K^T for one head, masked scores set to -inf.
 
-    q: (N_q, d), k: (N_k, d) -> (N_q, N_k) float64.
+    q: (N_q, d), k: (N_k, d) -> (N_q, N_k) float64.  ``hidden`` (bool (N_q, N_k)) hides
+    more keys on top of the causal mask.
     """
     s = scale * (np.asarray(q, np.float64) @ np.asarray(k, np.float64).T)
     if causal:
         s = np.where(causal_mask(s.shape[0], s.shape[1]), -np.inf, s)
+    if hidden is not None:
+        s = np.where(hidden, -np.inf, s)
     return s
 
 
@@ -90,38 +116,51 @@ def softmax_rows(s: np.ndarray):
     """Row-wise safe softmax of a score matrix ([FA-ch] 地基：流式 softmax).
 
     Subtracts the row max m before exponentiating so nothing overflows, then divides
-    by the row sum l.  Returns (P, m, l).  Rows may contain -inf (masked) entries but
-    at least one finite entry.
+    by the row sum l.  Returns (P, m, l).  Rows may contain -inf (masked) entries; a row
+    with no finite entry gets P = 0, m = -inf and l = 0.
     """
     s = np.asarray(s, np.float64)
     m = np.max(s, axis=-1, keepdims=True)
-    e = np.exp(s - m)
+    empty = ~np.isfinite(m)
+    e = np.exp(s - np.where(empty, 0.0, m))
     l = np.sum(e, axis=-1, keepdims=True)
-    return e / l, m[..., 0], l[..., 0]
+    p = e / np.where(empty, 1.0, l)
+    return p, m[..., 0], l[..., 0]
 
 
-def probabilities(q, k, scale: float, causal: bool) -> np.ndarray:
-    """P = softmax(scale * Q K^T) for one head (N x N, float64)."""
-    p, _, _ = softmax_rows(scores(q, k, scale, causal))
+def probabilities(q, k, scale: float, causal: bool, hidden=None) -> np.ndarray:
+    """P = softmax(scale * Q K^T) for one head (N_q x N_k, float64)."""
+    p, _, _ = softmax_rows(scores(q, k, scale, causal, hidden))
     return p
 
 
-def forward_head(q, k, v, scale: float, causal: bool):
-    """One head: returns (O (N, d), LSE (N,)) in float64."""
-    s = scores(q, k, scale, causal)
+def forward_head(q, k, v, scale: float, causal: bool, hidden=None):
+    """One head: returns (O (N_q, d), LSE (N_q,)) in float64; an empty row gives O = 0 and
+    LSE = -inf."""
+    s = scores(q, k, scale, causal, hidden)
     p, m, l = softmax_rows(s)
     o = p @ np.asarray(v, np.float64)
-    lse = m + np.log(l)
+    with np.errstate(divide="ignore"):
+        lse = m + np.log(l)
     return o, lse
 
 
-def forward(q, k, v, scale: float, causal: bool, heads=None):
+def _hidden(block_mask, h: int, n_q: int, n_k: int):
+    """Dense hidden-key mask of query head h from a (1 or H_q, nb_q, nb_k) block mask."""
+    if block_mask is None:
+        return None
+    bm = np.asarray(block_mask)
+    return expand_block_mask(bm[0 if bm.shape[0] == 1 else h], n_q, n_k)
+
+
+def forward(q, k, v, scale: float, causal: bool, heads=None, block_mask=None):
     """Attention forward: q (B, H_q, N_q, d), k and v (B, H_kv, N_k, d).
 
     Returns (O, LSE) as float64 arrays of shapes (B, H_q, N_q, d) and (B, H_q, N_q).
     With ``heads`` (an iterable of (b, h) query-head pairs) only those heads are
     computed and the other entries are NaN -- used to check sampled heads at full
-    problem sizes.
+    problem sizes.  ``block_mask`` ((1 or H_q, ceil(N_q/128), ceil(N_k/128)), 0 =
+    hidden block) applies a block-sparse mask.
     """
     q, k, v = np.asarray(q), np.asarray(k), np.asarray(v)
     B, H, N, d = q.shape
@@ -131,17 +170,18 @@ def forward(q, k, v, scale: float, causal: bool, heads=None):
     todo = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
     for b, h in todo:
         g = kv_head(h, H, Hkv)
-        o[b, h], lse[b, h] = forward_head(q[b, h], k[b, g], v[b, g], scale, causal)
+        hid = _hidden(block_mask, h, N, k.shape[2])
+        o[b, h], lse[b, h] = forward_head(q[b, h], k[b, g], v[b, g], scale, causal, hid)
     return o, lse
 
 
-def backward_head(q, k, v, do, scale: float, causal: bool):
+def backward_head(q, k, v, do, scale: float, causal: bool, hidden=None):
     """One head: returns (dQ, dK, dV) in float64 from Q, K, V and dO alone."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     do = np.asarray(do, np.float64)
-    p = probabilities(q, k, scale, causal)
+    p = probabilities(q, k, scale, causal, hidden)
     dv = p.T @ do
     dp = do @ v.T
     dsum = np.sum(p * dp, axis=-1, keepdims=True)  # D_i = sum_j P_ij dP_ij
@@ -151,7 +191,7 @@ def backward_head(q, k, v, do, scale: float, causal: bool):
     return dq, dk, dv
 
 
-def backward(q, k, v, do, scale: float, causal: bool, heads=None):
+def backward(q, k, v, do, scale: float, causal: bool, heads=None, block_mask=None):
     """Attention backward: q, dO (B, H_q, N_q, d), k, v (B, H_kv, N_k, d) ->
     (dQ, dK, dV) float64 in the shapes of q, k and v.
 
@@ -173,7 +213,8 @@ def backward(q, k, v, do, scale: float, causal: bool, heads=None):
         dk[b, g] = 0.0
         dv[b, g] = 0.0
         for h in range(g * G, (g + 1) * G):
-            dq[b, h], dkh, dvh = backward_head(q[b, h], k[b, g], v[b, g], do[b, h], scale, causal)
+            hid = _hidden(block_mask, h, N, k.shape[2])
+            dq[b, h], dkh, dvh = backward_head(q[b, h], k[b, g], v[b, g], do[b, h], scale, causal, hid)
             dk[b, g] += dkh
             dv[b, g] += dvh
     return dq, dk, dv

@@ -332,6 +332,112 @@ def pin_gqa_autograd(bwd_mh, causal, seed=27):
         np.testing.assert_allclose(x, t.grad.numpy(), rtol=0, atol=1e-10)
 
 
+# ------------------------------------------------ block-sparse masks, empty rows
+
+
+def _random_hidden(r, nq, nk, keep=0.6):
+    """A random hidden-key mask in which every query keeps at least one key."""
+    hid = r.random((nq, nk)) > keep
+    hid[np.arange(nq), r.integers(0, nk, nq)] = False
+    return hid
+
+
+def pin_mask_sdpa(fwd, nq=11, nk=23, d=6, seed=31):
+    """An arbitrary hidden-key mask against torch SDPA with the boolean attn_mask
+    (fp64, CPU); LSE against torch.logsumexp of the masked scores."""
+    r = _rng(seed)
+    q = r.standard_normal((nq, d))
+    k, v = (r.standard_normal((nk, d)) for _ in range(2))
+    hid = _random_hidden(r, nq, nk)
+    o, lse = fwd(q, k, v, 0.5, False, hid)
+    tq, tk, tv = (torch.from_numpy(a)[None, None] for a in (q, k, v))
+    keep = torch.from_numpy(~hid)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=keep, scale=0.5)[0, 0]
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+    sm = (torch.from_numpy(q) @ torch.from_numpy(k).T * 0.5).masked_fill(~keep, float("-inf"))
+    np.testing.assert_allclose(lse, torch.logsumexp(sm, dim=-1).numpy(), rtol=0, atol=1e-12)
+
+
+def pin_mask_autograd(bwd, nq=9, nk=14, d=4, seed=32):
+    """Gradients with an arbitrary hidden-key mask against autograd through fp64 SDPA."""
+    r = _rng(seed)
+    q, do = (r.standard_normal((nq, d)) for _ in range(2))
+    k, v = (r.standard_normal((nk, d)) for _ in range(2))
+    hid = _random_hidden(r, nq, nk)
+    tq, tk, tv = (torch.from_numpy(a)[None, None].requires_grad_(True) for a in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(~hid), scale=0.8)
+    out.backward(torch.from_numpy(do)[None, None])
+    dq, dk, dv = bwd(q, k, v, do, 0.8, False, hid)
+    for x, t in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(x, t.grad[0, 0].numpy(), rtol=0, atol=1e-10)
+
+
+def pin_empty_row(fwd, bwd, nq=7, nk=9, d=3, seed=33):
+    """A query row with every key hidden: O = 0, LSE = -inf and zero dQ; the other rows
+    are exactly what they are without that row, and dK, dV do not change."""
+    r = _rng(seed)
+    q, do = (r.standard_normal((nq, d)) for _ in range(2))
+    k, v = (r.standard_normal((nk, d)) for _ in range(2))
+    hid = _random_hidden(r, nq, nk)
+    hid[3] = True
+    o, lse = fwd(q, k, v, 0.6, False, hid)
+    assert np.all(o[3] == 0.0) and lse[3] == -np.inf
+    rest = [i for i in range(nq) if i != 3]
+    o2, lse2 = fwd(q[rest], k, v, 0.6, False, hid[rest])
+    np.testing.assert_array_equal(o[rest], o2)
+    np.testing.assert_array_equal(lse[rest], lse2)
+    dq, dk, dv = bwd(q, k, v, do, 0.6, False, hid)
+    assert np.all(dq[3] == 0.0)
+    dq2, dk2, dv2 = bwd(q[rest], k, v, do[rest], 0.6, False, hid[rest])
+    np.testing.assert_allclose(dk, dk2, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(dv, dv2, rtol=0, atol=1e-14)
+
+
+def pin_block_geometry(expand):
+    """128 x 128 blocks, ragged at the ends: a 2 x 3 block mask over 130 queries and 260
+    keys, checked at block edges and in the ragged last block."""
+    bm = np.array([[1, 0, 1], [0, 1, 0]], np.uint8)
+    hid = expand(bm, 130, 260)
+    assert hid.shape == (130, 260)
+    expect = {(0, 0): False, (127, 127): False, (127, 128): True, (128, 127): True, (128, 128): False,
+              (129, 255): False, (129, 256): True, (0, 256): False, (0, 259): False, (129, 259): True}
+    for (i, j), h in expect.items():
+        assert bool(hid[i, j]) == h, (i, j)
+    assert hid[:128, 128:256].all() and not hid[:128, :128].any()
+    try:
+        expand(bm, 257, 260)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("a block mask of the wrong shape must be rejected")
+
+
+def pin_block_sparse_causal(fwd_mh, seed=34):
+    """A block mask that keeps exactly the blocks on or below the diagonal changes
+    nothing under causal masking; an all-ones block mask changes nothing at all."""
+    r = _rng(seed)
+    B, H, N, d = 1, 2, 300, 4
+    q, k, v = (r.standard_normal((B, H, N, d)) for _ in range(3))
+    nb = -(-N // 128)
+    lower = np.tril(np.ones((nb, nb), np.uint8))[None]
+    o_c, l_c = fwd_mh(q, k, v, 0.5, True)
+    o_b, l_b = fwd_mh(q, k, v, 0.5, True, block_mask=lower)
+    np.testing.assert_array_equal(o_b, o_c)
+    np.testing.assert_array_equal(l_b, l_c)
+    ones = np.ones((H, nb, nb), np.uint8)
+    o_f, l_f = fwd_mh(q, k, v, 0.5, False)
+    o_1, l_1 = fwd_mh(q, k, v, 0.5, False, block_mask=ones)
+    np.testing.assert_array_equal(o_1, o_f)
+    np.testing.assert_array_equal(l_1, l_f)
+
+
+MASK_PINS = [
+    ("mask_sdpa", lambda f, b: pin_mask_sdpa(f)),
+    ("mask_autograd", lambda f, b: pin_mask_autograd(b)),
+    ("empty_row", lambda f, b: pin_empty_row(f, b)),
+]
+
+
 CROSS_FORWARD_PINS = [
     ("cross_sdpa", pin_cross_sdpa),
     ("causal_suffix", pin_causal_suffix),

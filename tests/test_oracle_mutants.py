@@ -10,7 +10,7 @@ import pytest
 
 from oracle import naive, tiled_ref
 from oracle_pins import (BACKWARD_PINS, CROSS_BACKWARD_PINS, CROSS_FORWARD_PINS, FORWARD_PINS, GQA_BACKWARD_PINS,
-                         GQA_FORWARD_PINS)
+                         GQA_FORWARD_PINS, MASK_PINS, pin_block_geometry)
 
 
 def _fwd(mut):
@@ -168,6 +168,35 @@ def test_gqa_mutants_are_caught():
     assert not _caught(GQA_BACKWARD_PINS, lambda pin: pin(_bwd_mh(None)))
     assert _caught(GQA_FORWARD_PINS, lambda pin: pin(_fwd_mh("head_mod")))
     assert _caught(GQA_BACKWARD_PINS, lambda pin: pin(_bwd_mh("no_group_sum")))
+
+
+def test_mask_mutants_are_caught():
+    """Blocks of 127 instead of 128 fail the geometry pin; a softmax that divides an empty
+    row by its zero sum (NaN instead of 0) fails the empty-row pin; ignoring the mask
+    fails the SDPA pin."""
+    def expand127(bm, n_q, n_k):
+        bm = np.asarray(bm)
+        keep = np.repeat(np.repeat(bm != 0, 127, axis=0), 127, axis=1)
+        if keep.shape[0] < n_q or keep.shape[1] < n_k:
+            raise AssertionError("too small")
+        return ~keep[:n_q, :n_k]
+    with pytest.raises(AssertionError):
+        pin_block_geometry(expand127)
+
+    def fwd_nan(q, k, v, scale, causal, hidden=None):
+        s = naive.scores(q, k, scale, causal, hidden)
+        m = s.max(axis=1, keepdims=True)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            e = np.exp(s - m)
+            l = e.sum(axis=1, keepdims=True)
+            return (e / l) @ v, (m + np.log(l))[:, 0]
+
+    def fwd_nomask(q, k, v, scale, causal, hidden=None):
+        return naive.forward_head(q, k, v, scale, causal)
+
+    assert _caught(MASK_PINS, lambda pin: pin(naive.forward_head, naive.backward_head)) == []
+    assert "empty_row" in _caught(MASK_PINS, lambda pin: pin(fwd_nan, naive.backward_head))
+    assert "mask_sdpa" in _caught(MASK_PINS, lambda pin: pin(fwd_nomask, naive.backward_head))
 
 
 def test_tiled_wrong_rescale_is_caught():

@@ -7,7 +7,7 @@ import pytest
 
 from oracle import naive, tiled_ref
 from oracle_pins import (BACKWARD_PINS, CROSS_BACKWARD_PINS, CROSS_FORWARD_PINS, FORWARD_PINS, GQA_BACKWARD_PINS,
-                         GQA_FORWARD_PINS, golden)
+                         GQA_FORWARD_PINS, MASK_PINS, golden, pin_block_geometry, pin_block_sparse_causal)
 
 
 @pytest.mark.parametrize("name,pin", FORWARD_PINS, ids=[n for n, _ in FORWARD_PINS])
@@ -38,6 +38,19 @@ def test_gqa_forward_pin(name, pin):
 @pytest.mark.parametrize("name,pin", GQA_BACKWARD_PINS, ids=[n for n, _ in GQA_BACKWARD_PINS])
 def test_gqa_backward_pin(name, pin):
     pin(naive.backward)
+
+
+@pytest.mark.parametrize("name,pin", MASK_PINS, ids=[n for n, _ in MASK_PINS])
+def test_mask_pin(name, pin):
+    pin(naive.forward_head, naive.backward_head)
+
+
+def test_block_geometry_pin():
+    pin_block_geometry(naive.expand_block_mask)
+
+
+def test_block_sparse_causal_pin():
+    pin_block_sparse_causal(naive.forward)
 
 
 def test_causal_rejects_more_queries_than_keys():
