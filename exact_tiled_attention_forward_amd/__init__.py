@@ -22,7 +22,7 @@ import os
 
 import torch  # the HIP runtime torch loads is the one libfa.so binds to (same soname)
 
-__all__ = ["fa_forward", "fa_forward_split_count", "fa_backward", "fa_backward_dq", "fa_backward_dkdv", "fa_backward_workspace_bytes",
+__all__ = ["MASK_BLOCK", "fa_forward", "fa_forward_split_count", "fa_backward", "fa_backward_dq", "fa_backward_dkdv", "fa_backward_workspace_bytes",
            "library", "FAError", "FA_F32", "FA_F16", "FA_BF16", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -74,6 +74,11 @@ def library() -> ctypes.CDLL:
     lib.fa_forward_split_workspace_bytes.restype = sz
     lib.fa_forward_split.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp, sz, i, vp]
     lib.fa_forward_split.restype = i
+    lib.fa_forward_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, i, i, vp, sz, i, vp]
+    lib.fa_forward_sparse.restype = i
+    lib.fa_backward_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, i, vp, i, i,
+                                       vp]
+    lib.fa_backward_sparse.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -124,7 +129,19 @@ def fa_forward_split_count(q, k, causal=False):
                                                 _DTYPE_CODE.get(q.dtype, -1)))
 
 
-def fa_forward(q, k, v, o=None, lse=None, *, scale=None, causal=False, stream=None, split=None, workspace=None):
+MASK_BLOCK = 128  # rows and columns of one block of a block-sparse mask
+
+
+def _block_mask(block_mask, Hq, Nq, Nk):
+    """Check a (1 or Hq, ceil(Nq/128), ceil(Nk/128)) uint8 GPU mask; returns (pointer, heads)."""
+    nb = ((Nq + MASK_BLOCK - 1) // MASK_BLOCK, (Nk + MASK_BLOCK - 1) // MASK_BLOCK)
+    if block_mask.dim() != 3 or tuple(block_mask.shape[1:]) != nb or block_mask.shape[0] not in (1, Hq):
+        raise ValueError(f"block_mask must be (1 or {Hq}, {nb[0]}, {nb[1]}) (got {tuple(block_mask.shape)})")
+    return _gpu_tensor("block_mask", block_mask, torch.uint8), int(block_mask.shape[0])
+
+
+def fa_forward(q, k, v, o=None, lse=None, *, scale=None, causal=False, stream=None, split=None, workspace=None,
+               block_mask=None):
     """O, lse = attention(q, k, v).
 
     q (B, Hq, Nq, d); k, v (B, Hkv, Nk, d) with Hq a multiple of Hkv (query head h
@@ -135,6 +152,9 @@ def fa_forward(q, k, v, o=None, lse=None, *, scale=None, causal=False, stream=No
     when the grid is too small to fill the GPU, e.g. a decode step), 1 forces one pass
     over the keys, n > 1 splits each query block's key range in up to n chunks merged
     afterwards.  ``workspace`` (uint8, optional) holds the split partials.
+
+    ``block_mask``: optional uint8 GPU tensor (1 or Hq, ceil(Nq/128), ceil(Nk/128)); a 0
+    byte hides a 128 x 128 block (see include/fa.h).
     """
     lib = library()
     B, Hq, Hkv, Nq, Nk, d = _shapes(q, k)
@@ -152,6 +172,17 @@ def fa_forward(q, k, v, o=None, lse=None, *, scale=None, causal=False, stream=No
     pl = _gpu_tensor("lse", lse, torch.float32, (B, Hq, Nq))
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     ns = fa_forward_split_count(q, k, causal) if split is None else int(split)
+    if block_mask is not None:
+        pm, mh = _block_mask(block_mask, Hq, Nq, Nk)
+        pw, nbytes = ctypes.c_void_p(0), 0
+        if ns > 1:
+            nbytes = int(lib.fa_forward_split_workspace_bytes(B, Hq, Nq, d, ns))
+            if workspace is None:
+                workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+            pw, nbytes = _gpu_tensor("workspace", workspace), workspace.numel() * workspace.element_size()
+        _check(lib.fa_forward_sparse(pq, pk, pv, po, pl, B, Hq, Hkv, Nq, Nk, d, ctypes.c_float(sc), int(bool(causal)),
+                                     pm, mh, max(ns, 1), pw, nbytes, _DTYPE_CODE[dt], _stream(stream, q.device)))
+        return o, lse
     if ns > 1:
         need = int(lib.fa_forward_split_workspace_bytes(B, Hq, Nq, d, ns))
         if workspace is None:
@@ -179,9 +210,9 @@ def _workspace(q, workspace):
 
 
 def fa_backward(q, k, v, o, do, lse, dq=None, dk=None, dv=None, *, scale=None, causal=False,
-                workspace=None, stream=None):
+                workspace=None, stream=None, block_mask=None):
     """dQ (like q), dK, dV (like k) as float32 gradients of sum(O * dO), recomputing P from
-    q, k and lse.  Shapes and grouping as for fa_forward."""
+    q, k and lse.  Shapes, grouping and block_mask as for fa_forward."""
     lib = library()
     B, Hq, Hkv, Nq, Nk, d = _shapes(q, k)
     dt, f32 = q.dtype, torch.float32
@@ -197,6 +228,12 @@ def fa_backward(q, k, v, o, do, lse, dq=None, dk=None, dv=None, *, scale=None, c
             _gpu_tensor("dk", dk, f32, k.shape), _gpu_tensor("dv", dv, f32, k.shape),
             _gpu_tensor("workspace", workspace)]
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if block_mask is not None:
+        pm, mh = _block_mask(block_mask, Hq, Nq, Nk)
+        _check(lib.fa_backward_sparse(*ptrs, workspace.numel() * workspace.element_size(), B, Hq, Hkv, Nq, Nk, d,
+                                      ctypes.c_float(sc), int(bool(causal)), pm, mh, _DTYPE_CODE[dt],
+                                      _stream(stream, q.device)))
+        return dq, dk, dv
     _check(lib.fa_backward_ex(*ptrs, workspace.numel() * workspace.element_size(), B, Hq, Hkv, Nq, Nk, d,
                               ctypes.c_float(sc), int(bool(causal)), _DTYPE_CODE[dt], _stream(stream, q.device)))
     return dq, dk, dv

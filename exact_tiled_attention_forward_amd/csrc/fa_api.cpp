@@ -98,6 +98,32 @@ int fa_forward_split(const void* q, const void* k, const void* v, void* o, float
   return FA_OK;
 }
 
+int fa_forward_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                      int Nq, int Nk, int d, float scale, int causal, const void* block_mask, int mask_heads,
+                      int nsplit, void* workspace, size_t workspace_bytes, fa_dtype_t dtype, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse || !block_mask) return FA_ERR_NULL;
+  if (nsplit < 1 || nsplit > kMaxSplits) return FA_ERR_SHAPE;
+  int st = check_shape(B, Hq, Hkv, Nq, Nk, d, (int)dtype, causal);
+  if (st != FA_OK) return st;
+  if (mask_heads != 1 && mask_heads != Hq) return FA_ERR_SHAPE;
+  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hq * ((Nq + 31) / 32 + 1) * nsplit >= (int64_t)1 << 31) return FA_ERR_SHAPE;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse)) return FA_ERR_ALIGN;
+  if (nsplit > 1) {
+    if (!workspace || workspace_bytes < fa::fwd_split_bytes(B, Hq, Nq, d, nsplit)) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  }
+  fa::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal != 0, (int)dtype, stream};
+  a.nsplit = nsplit;
+  a.part = nsplit > 1 ? (float*)workspace : nullptr;
+  a.bmask = (const uint8_t*)block_mask;
+  a.mask_heads = mask_heads;
+  (void)hipGetLastError();
+  if (fa::launch_forward(a) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
 int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N, int d,
                float scale, int causal, fa_dtype_t dtype, hipStream_t stream) {
   return fa_forward_ex(q, k, v, o, lse, B, H, H, N, N, d, scale, causal, dtype, stream);
@@ -131,9 +157,12 @@ int check_backward(const void* q, const void* k, const void* v, const void* o, c
 
 int run_backward(const void* q, const void* k, const void* v, const void* dO, const float* lse, float* dq,
                  float* dk, float* dv, void* workspace, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
-                 int causal, fa_dtype_t dtype, hipStream_t stream, int stages) {
+                 int causal, fa_dtype_t dtype, hipStream_t stream, int stages, const void* block_mask = nullptr,
+                 int mask_heads = 0) {
   fa::BwdArgs a{q, k, v, nullptr, dO, lse, dq, dk, dv, (float*)workspace, B, Hq, Hkv, Nq, Nk, d, scale, causal != 0,
                 (int)dtype, stream};
+  a.bmask = (const uint8_t*)block_mask;
+  a.mask_heads = mask_heads;
   (void)hipGetLastError();
   if (fa::launch_backward(a, stages) != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
@@ -171,6 +200,19 @@ int fa_backward_dkdv_ex(const void* q, const void* k, const void* v, const void*
   if (st != FA_OK) return st;
   return run_backward(q, k, v, dO, nullptr, nullptr, dk, dv, const_cast<void*>(workspace), B, Hq, Hkv, Nq, Nk, d,
                       scale, causal, dtype, stream, fa::kStageDkdv);
+}
+
+int fa_backward_sparse(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                       float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes, int B, int Hq,
+                       int Hkv, int Nq, int Nk, int d, float scale, int causal, const void* block_mask,
+                       int mask_heads, fa_dtype_t dtype, hipStream_t stream) {
+  if (!block_mask) return FA_ERR_NULL;
+  const int st = check_backward(q, k, v, o, dO, lse, dq, dk, dv, workspace, workspace_bytes, B, Hq, Hkv, Nq, Nk, d,
+                                scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (mask_heads != 1 && mask_heads != Hq) return FA_ERR_SHAPE;
+  return run_backward(q, k, v, dO, lse, dq, dk, dv, workspace, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, stream,
+                      fa::kStageDq | fa::kStageDkdv, block_mask, mask_heads);
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,

@@ -32,16 +32,24 @@
 
 namespace fa {
 
+// Block-sparse mask as the kernels see it: (mask heads, ceil(Nq/128), ceil(Nk/128)) bytes,
+// 0 = hidden 128 x 128 block; query head h (index within the batch) reads layer
+// h * hstride (0: one layer shared by every head).
+struct BwdMask {
+  const uint8_t* bytes;
+  int Hq, hstride, nbk;
+};
+constexpr int kMaskBlock = 128;
+
 // ----------------------------------------------------------------------------------
 // 1. dQ (and D, lse2).  NW waves x 32 queries per workgroup; BC keys per tile.
 // ----------------------------------------------------------------------------------
-template <class T, int D, int NW, int BC, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                                                         const uint16_t* __restrict__ V,
-                                                         const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
-                                                         float* __restrict__ delta, float* __restrict__ lse2,
-                                                         float* __restrict__ dQ, int BH, int G, int Nq, int Nk,
-                                                         float c, float scale) {
+template <class T, int D, int NW, int BC, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ delta,
+    float* __restrict__ lse2, float* __restrict__ dQ, int BH, int G, int Nq, int Nk, float c, float scale,
+    const BwdMask mask) {
   constexpr int BR = 32 * NW;
   constexpr int NT = NW * 64;
   constexpr int TB = BC * D * 2;
@@ -86,19 +94,35 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
   for (int db = 0; db < DB; ++db) dq[db] = (f32x16){};
 
+  // block-sparse: the workgroup's rows form one 128-row mask block; key tiles in hidden
+  // blocks are neither loaded nor computed
+  static_assert(!SPARSE || (kMaskBlock % BR == 0 && kMaskBlock % BC == 0), "tiles inside mask blocks");
+  const uint8_t* mrow = SPARSE ? mask.bytes + (size_t)(bh % mask.Hq) * mask.hstride +
+                                     (size_t)(q0 / kMaskBlock) * mask.nbk
+                               : nullptr;
+  auto next_tile = [&](int j) {
+    if (SPARSE)
+      while (j < nkt && !mrow[(j * BC) / kMaskBlock]) ++j;
+    return j;
+  };
+
   for (int pass = 0; pass < 2; ++pass) {
     __syncthreads();  // the previous pass is done with both LDS buffers
-    tile_load_async<D, BC, NT>(lds, rk, 0, tid);
-    tile_load_async<D, BC, NT>(lds + 2 * TB, rv, 0, tid);
-    for (int j = 0; j < nkt; ++j) {
+    int j = next_tile(0);
+    if (j < nkt) {
+      tile_load_async<D, BC, NT>(lds, rk, j * BC, tid);
+      tile_load_async<D, BC, NT>(lds + 2 * TB, rv, j * BC, tid);
+    }
+    for (int cur = 0; j < nkt; cur ^= 1) {
       wait_vmem();
       __syncthreads();
-      const int cur = j & 1;
-      if (j + 1 < nkt) {
-        tile_load_async<D, BC, NT>(lds + (cur ^ 1) * TB, rk, (j + 1) * BC, tid);
-        tile_load_async<D, BC, NT>(lds + (2 + (cur ^ 1)) * TB, rv, (j + 1) * BC, tid);
+      const int jn = next_tile(j + 1);
+      if (jn < nkt) {
+        tile_load_async<D, BC, NT>(lds + (cur ^ 1) * TB, rk, jn * BC, tid);
+        tile_load_async<D, BC, NT>(lds + (2 + (cur ^ 1)) * TB, rv, jn * BC, tid);
       }
       const int k0 = j * BC;
+      j = jn;
       if (CAUSAL && k0 > qw0 + 31 + off) continue;
       const FA_LDS uint8_t* kt = lds + cur * TB;
       const FA_LDS uint8_t* vt = lds + (2 + cur) * TB;
@@ -180,11 +204,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // products run on the matrix core.  Per tile: barrier (Q, dO, statistics in LDS), A
 // computes and publishes P while B computes dP, barrier, both finish their products.
 // ----------------------------------------------------------------------------------
-template <class T, int D, int NP, int BQ, bool CAUSAL>
+template <class T, int D, int NP, int BQ, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ delta, const float* __restrict__ lse2,
-    float* __restrict__ dK, float* __restrict__ dV, int BHkv, int G, int Nq, int Nk, float c, float scale) {
+    float* __restrict__ dK, float* __restrict__ dV, int BHkv, int G, int Nq, int Nk, float c, float scale,
+    const BwdMask mask) {
   constexpr int NW = 2 * NP;
   constexpr int BKV = 32 * NP;
   constexpr int NT = NW * 64;
@@ -236,7 +261,22 @@ __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(2, 
     }
   };
 
-  if (ntiles > 0) load_tile(0, 0);
+  // block-sparse: the workgroup's keys form one 128-key mask block, each query tile lies in
+  // one 128-row block: hidden tiles are neither loaded nor computed
+  static_assert(!SPARSE || (BKV == kMaskBlock && kMaskBlock % BQ == 0), "tiles inside mask blocks");
+  auto next_tile = [&](int t) {
+    if (SPARSE) {
+      const int hbase = (bkv % (mask.Hq / G)) * G;  // the group's first query head within the batch
+      for (; t < ntiles; ++t) {
+        const int hq = hbase + t / nt;
+        const int qblk = ((qt0 + t % nt) * BQ) / kMaskBlock;
+        if (mask.bytes[(size_t)hq * mask.hstride + (size_t)qblk * mask.nbk + k0 / kMaskBlock]) break;
+      }
+    }
+    return t;
+  };
+  int t = next_tile(0);
+  if (t < ntiles) load_tile(t, 0);
 
   // this wave's keys (A) or values (B) as B operands (lane = key, 8 consecutive d per lane)
   u32x4 kv[DS];
@@ -250,12 +290,13 @@ __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = (f32x16){};
 
-  for (int t = 0; t < ntiles; ++t) {
+  for (int cur = 0; t < ntiles; cur ^= 1) {
     wait_vmem();
     __syncthreads();
-    const int cur = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1, cur ^ 1);
+    const int tn = next_tile(t + 1);
+    if (tn < ntiles) load_tile(tn, cur ^ 1);
     const int q0 = (qt0 + t % nt) * BQ;
+    t = tn;
     // every query of the tile precedes this pair's keys: P = 0 (both waves of the pair
     // agree, and both still meet the barrier below)
     const bool active = !(CAUSAL && q0 + BQ - 1 + off < kw0);
@@ -357,8 +398,10 @@ constexpr int kNWq = 4, kBCq = 32;
 // 64 queries per streamed Q/dO tile: two accumulator blocks per wave between barriers
 constexpr int kBQkv = 64;
 
-template <class T, int D, bool CAUSAL>
+template <class T, int D, bool CAUSAL, bool SPARSE>
 hipError_t go(const BwdArgs& a, int stages) {
+  const int nbq = (a.Nq + kMaskBlock - 1) / kMaskBlock, nbk = (a.Nk + kMaskBlock - 1) / kMaskBlock;
+  const BwdMask mask{a.bmask, a.Hq, a.mask_heads == 1 ? 0 : nbq * nbk, nbk};
   const int BHq = a.B * a.Hq;
   const int BHkv = a.B * a.Hkv;
   const int G = a.Hq / a.Hkv;
@@ -369,21 +412,27 @@ hipError_t go(const BwdArgs& a, int stages) {
   if (stages & kStageDq) {
     constexpr int BR = 32 * kNWq;
     const int nqb = (a.Nq + BR - 1) / BR;
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, kNWq, kBCq, CAUSAL>), dim3(BHq * nqb), dim3(kNWq * 64), 0, a.stream,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (const uint16_t*)a.dO,
-                       a.lse, delta, lse2, a.dq, BHq, G, a.Nq, a.Nk, c, a.scale);
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, kNWq, kBCq, CAUSAL, SPARSE>), dim3(BHq * nqb), dim3(kNWq * 64), 0,
+                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                       (const uint16_t*)a.dO, a.lse, delta, lse2, a.dq, BHq, G, a.Nq, a.Nk, c, a.scale, mask);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & kStageDkdv) {
     constexpr int BKV = 32 * kNPkv;
     const int nkb = (a.Nk + BKV - 1) / BKV;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kNPkv, kBQkv, CAUSAL>), dim3(BHkv * nkb), dim3(2 * kNPkv * 64), 0,
-                       a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                       (const uint16_t*)a.dO, delta, lse2, a.dk, a.dv, BHkv, G, a.Nq, a.Nk, c, a.scale);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kNPkv, kBQkv, CAUSAL, SPARSE>), dim3(BHkv * nkb),
+                       dim3(2 * kNPkv * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (const uint16_t*)a.dO, delta, lse2, a.dk, a.dv, BHkv, G, a.Nq, a.Nk, c,
+                       a.scale, mask);
     return hipGetLastError();
   }
   return hipSuccess;
+}
+
+template <class T, int D, bool CAUSAL>
+hipError_t go(const BwdArgs& a, int stages) {
+  return a.bmask ? go<T, D, CAUSAL, true>(a, stages) : go<T, D, CAUSAL, false>(a, stages);
 }
 
 template <int D>

@@ -90,7 +90,33 @@ struct Fwd16Params {
   int ct;               // key tiles per split (>= every block's tile count: no split)
   int nsplit;           // splits the partial buffer holds
   float* part;          // split partials: o [s][row][D], then m, l, lr [s][row]
+  // block-sparse mask: (mask heads, nbq, nbk) bytes, 0 = hidden 128 x 128 block; a
+  // query head's layer is at its index within the batch times bm_hstride (0: shared)
+  const uint8_t* bmask;
+  int Hkv, bm_hstride, nbk;
 };
+
+constexpr int kMaskBlock = 128;  // rows and columns of one block of a block-sparse mask
+
+// Does any packed row in [r0, r1) of key/value head bkv need key tile j (tile keys
+// [j*BC, j*BC + BC), inside one mask block because BC divides 128)?  Walks the rows in
+// segments that share a query head and a 128-row mask block.
+template <int BC>
+__device__ __forceinline__ bool rows_need_tile(const Fwd16Params& P, int bkv, int r0, int r1, int j) {
+  static_assert(kMaskBlock % BC == 0, "a key tile must lie inside one mask block");
+  const int kblk = (j * BC) / kMaskBlock;
+  const int hbase = (bkv % P.Hkv) * P.G;  // the group's first query head within the batch
+  const int nbq = (P.Nq + kMaskBlock - 1) / kMaskBlock;
+  for (int r = r0; r < r1;) {
+    const int pos = r % P.Nq;
+    const int hq = hbase + r / P.Nq;
+    if (P.bmask[(size_t)hq * P.bm_hstride + (size_t)(pos / kMaskBlock) * P.nbk + kblk]) return true;
+    const int step = min(kMaskBlock - pos % kMaskBlock, P.Nq - pos);
+    r += step;
+  }
+  (void)nbq;
+  return false;
+}
 
 // Merge of the split partials of one packed row with the (m, l) rule of the tiled
 // method ("FlashAttention：IO 感知…", 基准/方法设计): with M = max_s m_s and
@@ -110,7 +136,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_merge_kernel(const Fwd16Params P)
   const float* pl = pm + (size_t)P.nsplit * nrows;
   const float* plr = pl + (size_t)P.nsplit * nrows;
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[s * nrows + g]);  // finite: split 0 holds key 0
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[s * nrows + g]);  // -inf only for a row with no visible key
   constexpr int E = D / 64;
   float acc[E] = {};
   float lt = 0.f, lr = 0.f;
@@ -123,7 +149,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_merge_kernel(const Fwd16Params P)
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] += a * po[e];
   }
-  const float inv = 1.0f / lr;
+  const float inv = lr > 0.f ? 1.0f / lr : 0.f;
   uint16_t* orow = P.O + g * D + E * lane;
   if constexpr (E == 2) {
     *(uint32_t*)orow = T::pack(acc[0] * inv, acc[1] * inv);
@@ -131,10 +157,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_merge_kernel(const Fwd16Params P)
     const uint32_t w = T::pack(acc[0] * inv, 0.f);
     *orow = (uint16_t)(w & 0xffffu);
   }
-  if (lane == 0) P.LSE[g] = (M + log2f(lt)) * kLn2;
+  if (lane == 0) P.LSE[g] = lt > 0.f ? (M + log2f(lt)) * kLn2 : -INFINITY;
 }
 
-template <class T, int D, int NW, int BC, int WPE, bool CAUSAL, bool SPLIT>
+template <class T, int D, int NW, int BC, int WPE, bool CAUSAL, bool SPLIT, bool SPARSE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void fwd16_kernel(
     const Fwd16Params P) {
   constexpr int BR = 32 * NW;
@@ -176,8 +202,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const auto rk = make_rsrc(P.K + kvhead, (uint32_t)Nk * D * 2);
   const auto rv = make_rsrc(P.V + kvhead, (uint32_t)Nk * D * 2);
 
-  tile_load_async<D, BC, NT>(lds, rk, j0 * BC, tid);
-  tile_load_async<D, BC, NT>(lds + 2 * TB, rv, j0 * BC, tid);
+  // block-sparse: tiles no row of the workgroup needs are neither loaded nor computed
+  const int rend = min(q0 + BR, R);
+  auto next_tile = [&](int j) {
+    if (SPARSE)
+      while (j < j1 && !rows_need_tile<BC>(P, bkv, q0, rend, j)) ++j;
+    return j;
+  };
+  // this lane's row of the mask (its query head and 128-row block)
+  const uint8_t* mrow = nullptr;
+  if (SPARSE) {
+    const int r = qrow < R ? qrow : q0;
+    mrow = P.bmask + (size_t)((bkv % P.Hkv) * P.G + r / Nq) * P.bm_hstride +
+           (size_t)((r % Nq) / kMaskBlock) * P.nbk;
+  }
+
+  int j = next_tile(j0);
+  if (j < j1) {
+    tile_load_async<D, BC, NT>(lds, rk, j * BC, tid);
+    tile_load_async<D, BC, NT>(lds + 2 * TB, rv, j * BC, tid);
+  }
 
   u32x4 qf[DS];
 #pragma unroll
@@ -192,16 +236,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
 
-  for (int j = j0; j < j1; ++j) {
+  for (int cur = 0; j < j1; cur ^= 1) {
     wait_vmem();
     __syncthreads();
-    const int cur = (j - j0) & 1;
-    if (j + 1 < j1) {
-      tile_load_async<D, BC, NT>(lds + (cur ^ 1) * TB, rk, (j + 1) * BC, tid);
-      tile_load_async<D, BC, NT>(lds + (2 + (cur ^ 1)) * TB, rv, (j + 1) * BC, tid);
+    const int jn = next_tile(j + 1);
+    if (jn < j1) {
+      tile_load_async<D, BC, NT>(lds + (cur ^ 1) * TB, rk, jn * BC, tid);
+      tile_load_async<D, BC, NT>(lds + (2 + (cur ^ 1)) * TB, rv, jn * BC, tid);
     }
     const int k0 = j * BC;
+    j = jn;
     if (!wave_rows || (CAUSAL && k0 > wpmax + off)) continue;  // no row of the wave sees the tile
+    bool lane_keep = true;  // block-sparse: this lane's row keeps the tile's mask block
+    bool mask_lanes = false;
+    if (SPARSE) {
+      lane_keep = mrow[k0 / kMaskBlock] != 0;
+      const uint64_t keep = __builtin_amdgcn_ballot_w64(lane_keep);
+      if (keep == 0) continue;
+      mask_lanes = keep != ~0ull;
+    }
     const FA_LDS uint8_t* kt = lds + cur * TB;
     const FA_LDS uint8_t* vt = lds + (2 + cur) * TB;
 
@@ -214,14 +267,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       for (int st = 0; st < DS; ++st) s[kb] = T::mfma(lds_row16<D>(kt, 32 * kb + c32, 2 * st + half), qf[st], s[kb]);
     }
 
-    // masks: keys past the end, and (causal) keys after the query's position
-    if ((k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > wpmin + off)) {
+    // masks: keys past the end, (causal) keys after the query's position, and
+    // (block-sparse) rows whose mask block is 0
+    if ((k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > wpmin + off) || mask_lanes) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + 32 * kb + acc_row(i, half);
-          s[kb][i] = (key >= Nk || (CAUSAL && key > pos + off)) ? -INFINITY : s[kb][i];
+          s[kb][i] = (!lane_keep || key >= Nk || (CAUSAL && key > pos + off)) ? -INFINITY : s[kb][i];
         }
     }
 
@@ -294,8 +348,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   }
   // epilogue: one division per row, 16-bit O, natural-log LSE.  O divides by the sum of
   // the rounded probabilities the P V product used, which makes it an exact weighted
-  // average of V rows; the logsumexp uses the fp32 sum.
-  const float inv = 1.0f / ltr;
+  // average of V rows; the logsumexp uses the fp32 sum.  A row with no visible key (only
+  // under a block-sparse mask) gets O = 0 and lse = -inf.
+  const float inv = ltr > 0.f ? 1.0f / ltr : 0.f;
   uint16_t* orow = P.O + head + (size_t)qrow * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -307,7 +362,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       w.y = T::pack(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
       *(u32x2*)(orow + d) = w;
     }
-  if (half == 0) P.LSE[(size_t)bkv * R + qrow] = (m + log2f(lt)) * kLn2;
+  if (half == 0) P.LSE[(size_t)bkv * R + qrow] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
 }
 
 // ----------------------------------------------------------------------------------
@@ -461,18 +516,20 @@ template <>
 struct Fwd16Shape<64> { static constexpr int NW = 8, BC = 64, WPE = 4; };
 constexpr int kNW32 = 2, kBC32 = 32;
 
-template <class T, int D, bool CAUSAL>
+template <class T, int D, bool CAUSAL, bool SPARSE>
 hipError_t go16(const FwdArgs& a) {
   using S = Fwd16Shape<D>;
   constexpr int BR = 32 * S::NW;
   const int R = (a.Hq / a.Hkv) * a.Nq;
   const int nqb = (R + BR - 1) / BR;
   const int BHkv = a.B * a.Hkv;
+  const int nbq = (a.Nq + kMaskBlock - 1) / kMaskBlock, nbk = (a.Nk + kMaskBlock - 1) / kMaskBlock;
   Fwd16Params p{(const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
-                BHkv, a.Hq / a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, 0, 1, nullptr};
+                BHkv, a.Hq / a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, 0, 1, nullptr,
+                a.bmask, a.Hkv, a.mask_heads == 1 ? 0 : nbq * nbk, nbk};
   if (a.nsplit <= 1) {
     p.ct = (a.Nk + S::BC - 1) / S::BC;
-    hipLaunchKernelGGL((fwd16_kernel<T, D, S::NW, S::BC, S::WPE, CAUSAL, false>), dim3(BHkv * nqb),
+    hipLaunchKernelGGL((fwd16_kernel<T, D, S::NW, S::BC, S::WPE, CAUSAL, false, SPARSE>), dim3(BHkv * nqb),
                        dim3(S::NW * 64), 0, a.stream, p);
     return hipGetLastError();
   }
@@ -486,7 +543,7 @@ hipError_t go16(const FwdArgs& a) {
   const int ns = (max_tiles + p.ct - 1) / p.ct;
   p.nsplit = a.nsplit;
   p.part = a.part;
-  hipLaunchKernelGGL((fwd16_kernel<T, D, S::NW, S::BC, S::WPE, CAUSAL, true>), dim3(BHkv * nqb * ns),
+  hipLaunchKernelGGL((fwd16_kernel<T, D, S::NW, S::BC, S::WPE, CAUSAL, true, SPARSE>), dim3(BHkv * nqb * ns),
                      dim3(S::NW * 64), 0, a.stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -495,6 +552,11 @@ hipError_t go16(const FwdArgs& a) {
   hipLaunchKernelGGL((fwd_merge_kernel<T, D, NWM, BR, S::BC, CAUSAL>), dim3((nrows + NWM - 1) / NWM), dim3(NWM * 64),
                      0, a.stream, p);
   return hipGetLastError();
+}
+
+template <class T, int D, bool CAUSAL>
+hipError_t go16(const FwdArgs& a) {
+  return a.bmask ? go16<T, D, CAUSAL, true>(a) : go16<T, D, CAUSAL, false>(a);
 }
 
 template <int D, bool CAUSAL>

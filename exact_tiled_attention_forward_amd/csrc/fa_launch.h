@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime_api.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace fa {
 
@@ -25,6 +26,8 @@ struct FwdArgs {
   hipStream_t stream;
   int nsplit = 1;          // > 1: split each query block's key range (16-bit inputs only)
   float* part = nullptr;   // workspace for the split partials (fwd_split_bytes)
+  const uint8_t* bmask = nullptr;  // block-sparse mask (mask_heads, ceil(Nq/128), ceil(Nk/128))
+  int mask_heads = 0;              // 1 (shared) or Hq
 };
 
 // Bytes of the split partials: nsplit x (B*Hq*Nq rows) x (d + 3) floats.
@@ -54,6 +57,8 @@ struct BwdArgs {
   bool causal;
   int dtype;
   hipStream_t stream;
+  const uint8_t* bmask = nullptr;  // block-sparse mask, as in FwdArgs
+  int mask_heads = 0;
 };
 
 constexpr int kStageDq = 1;    // dQ kernel (also writes D and lse*log2(e))

@@ -214,6 +214,34 @@ int fa_forward_split(const void* q, const void* k, const void* v, void* o, float
                      int nsplit, void* workspace, size_t workspace_bytes,
                      fa_dtype_t dtype, hipStream_t stream);
 
+/*
+ * Block-sparse masks
+ * ------------------
+ * Block-sparse attention ("FlashAttention：IO 感知…", 方法细节, and its long-range
+ * results) skips whole zero blocks of a given block mask.  block_mask is a device array
+ * of uint8 with shape (mask_heads, ceil(Nq/128), ceil(Nk/128)), row-major, shared by
+ * every batch element; mask_heads is 1 (one layer for every query head) or Hq (one per
+ * query head).  Byte (h, i, j) == 0 hides keys 128j .. 128j+127 from queries
+ * 128i .. 128i+127 of query head h, on top of the causal mask.  Hidden blocks are
+ * neither loaded nor computed.  A query row left with no visible key gets O = 0,
+ * lse = -inf and zero gradients.  Other arguments as for fa_forward_split /
+ * fa_backward_ex (nsplit >= 1; the workspace only for nsplit > 1); 16-bit inputs only
+ * (FA_ERR_UNSUPPORTED for fp32); mask_heads not 1 or Hq is FA_ERR_SHAPE; a NULL mask is
+ * FA_ERR_NULL.  The mask must not change between the forward and backward calls.
+ */
+int fa_forward_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                      const void* block_mask, int mask_heads, int nsplit,
+                      void* workspace, size_t workspace_bytes,
+                      fa_dtype_t dtype, hipStream_t stream);
+
+int fa_backward_sparse(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                       const float* lse, float* dq, float* dk, float* dv,
+                       void* workspace, size_t workspace_bytes,
+                       int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                       const void* block_mask, int mask_heads,
+                       fa_dtype_t dtype, hipStream_t stream);
+
 /* fa_status_string -- static, human-readable text for a status code. */
 const char* fa_status_string(int status);
 

@@ -186,3 +186,19 @@ def test_split_entry_points_validate_before_launch():
     assert lib.fa_forward_split(*args, 4, P2, need, fa.FA_F32, NUL) == FA_ERR_UNSUPPORTED
     bad = (P, P, P, P2, P2, 1, 4, 3, 1, 512, 128, ctypes.c_float(0.125), 1)
     assert lib.fa_forward_split(*bad, 4, P2, need, fa.FA_BF16, NUL) == FA_ERR_SHAPE
+
+
+@needs_lib
+def test_sparse_entry_points_validate_before_launch():
+    lib = fa.library()
+    base = (P, P, P, P2, P2, 1, 4, 2, 256, 256, 64, ctypes.c_float(0.125), 1)
+    assert lib.fa_forward_sparse(*base, NUL, 1, 1, NUL, 0, fa.FA_BF16, NUL) == FA_ERR_NULL
+    assert lib.fa_forward_sparse(*base, P, 3, 1, NUL, 0, fa.FA_BF16, NUL) == FA_ERR_SHAPE   # heads not 1 or Hq
+    assert lib.fa_forward_sparse(*base, P, 1, 0, NUL, 0, fa.FA_BF16, NUL) == FA_ERR_SHAPE   # nsplit < 1
+    assert lib.fa_forward_sparse(*base, P, 1, 1, NUL, 0, fa.FA_F32, NUL) == FA_ERR_UNSUPPORTED
+    assert lib.fa_forward_sparse(*base, P, 4, 2, NUL, 0, fa.FA_BF16, NUL) == FA_ERR_WORKSPACE
+    need = lib.fa_backward_workspace_bytes(1, 4, 256, 64)
+    bargs = (P, P, P, P, P, P2, P2, P2, P2, P2, need, 1, 4, 2, 256, 256, 64, ctypes.c_float(0.125), 1)
+    assert lib.fa_backward_sparse(*bargs, NUL, 1, fa.FA_BF16, NUL) == FA_ERR_NULL
+    assert lib.fa_backward_sparse(*bargs, P, 2, fa.FA_BF16, NUL) == FA_ERR_SHAPE
+    assert lib.fa_backward_sparse(*bargs, P, 1, fa.FA_F32, NUL) == FA_ERR_UNSUPPORTED
