@@ -232,7 +232,8 @@ def sweep(names, reps: int, out_path: str):
     cache, again with a 512 MB fill between launches ("cold")."""
     import torch
     import exact_tiled_attention_forward_amd as fa
-    from exact_tiled_attention_forward_amd.workloads import WORKLOADS, workload_inputs, elem_bytes
+    from exact_tiled_attention_forward_amd.workloads import (WORKLOADS, elem_bytes, local_global_block_mask,
+                                                             workload_inputs)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -248,8 +249,12 @@ def sweep(names, reps: int, out_path: str):
         if ns > 1:
             nbytes = fa.library().fa_forward_split_workspace_bytes(w.B, w.H, w.N, w.d, ns)
             wsf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        bm = local_global_block_mask(w.N).to(dev) if name == "block_sparse_local" else None
         passes = {"fwd": lambda: fa.fa_forward(q, k, v, o, lse, causal=w.causal, stream=stream, split=ns,
-                                               workspace=wsf)}
+                                               workspace=wsf, block_mask=bm)}
+        if bm is not None:
+            passes["fwd dense"] = lambda: fa.fa_forward(q, k, v, o, lse, causal=w.causal, stream=stream, split=ns,
+                                                        workspace=wsf)
         if w.backward:
             do = inp["do"].to(dev)
             f32 = torch.float32
@@ -258,13 +263,17 @@ def sweep(names, reps: int, out_path: str):
             ws = torch.empty(fa.fa_backward_workspace_bytes(w.B, w.H, w.N, w.d), dtype=torch.uint8, device=dev)
             passes["fwd"]()
             passes["bwd"] = lambda: fa.fa_backward(q, k, v, o, do, lse, dq, dk, dv, causal=w.causal, workspace=ws,
-                                                 stream=stream)
+                                                 stream=stream, block_mask=bm)
+            if bm is not None:
+                passes["bwd dense"] = lambda: fa.fa_backward(q, k, v, o, do, lse, dq, dk, dv, causal=w.causal,
+                                                             workspace=ws, stream=stream)
         s = elem_bytes(w.dtype)
         unit = 2.0 * w.B * w.H * w.visible_pairs() * w.d
         qrows, kvrows = w.B * w.H * w.N, w.B * w.Hkv * w.Nk
         info = {"fwd": (2 * unit, qrows * (2 * w.d * s + 4) + kvrows * 2 * w.d * s),
                 "bwd": (5 * unit, qrows * (3 * w.d * s + 4 * w.d + 8) + kvrows * (2 * w.d * s + 8 * w.d)),
                 "3step": (2 * unit, qrows * (2 * w.d * s + 4) + kvrows * 2 * w.d * s)}
+        info["fwd dense"], info["bwd dense"] = info["fwd"], info["bwd"]
         if w.N <= 16:
             # the plain three-step path for comparison: S = Q K^T, softmax, P V as library calls
             G = w.H // w.Hkv
@@ -296,6 +305,8 @@ def sweep(names, reps: int, out_path: str):
                 ts.sort()
                 med, mn = ts[len(ts) // 2], ts[0]
                 flops, nbytes = info[pname]
+                if bm is not None and pname in ("fwd", "bwd"):
+                    flops *= float(bm.float().mean())  # the visible blocks' share of the work
                 shape = f"{w.B}x{w.H}x{w.N}x{w.d}" if (w.Hkv, w.Nk) == (w.H, w.N) else \
                     f"{w.B}x{w.H}/{w.Hkv}x{w.N}/{w.Nk}x{w.d}"
                 rows.append({"workload": name, "shape": shape, "dtype": w.dtype,
@@ -315,7 +326,8 @@ def sweep(names, reps: int, out_path: str):
                 "algorithmic bytes (inputs read once, outputs written once) over the median time.  cold = a "
                 "512 MB fill between launches.  Shapes with a slash are query/key-value heads and query/key rows; "
                 "3step is the plain S = QK^T, softmax, PV path as three library calls (torch matmul and softmax), "
-                "timed for comparison on decode shapes.\n\n")
+                "timed for comparison on decode shapes.  block_sparse_local runs under its block mask (TFLOP/s "
+                "count the visible blocks only) and again dense for comparison.\n\n")
         f.write("| workload | B x H x N x d | dtype | causal | pass | mode | median (us) | min (us) | TFLOP/s "
                 "| % peak | GB/s |\n|---|---|---|---|---|---|---|---|---|---|---|\n")
         for r in rows:
@@ -408,7 +420,7 @@ def main():
 
     if args.sweep:
         names = ["single_head_f32", "prefill_bf16", "gpt2_medium_train", "long_f16", "long_bf16", "large_head_causal",
-                 "gqa_causal_train", "decode_gqa"]
+                 "gqa_causal_train", "decode_gqa", "block_sparse_local"]
         log("wrote", sweep(names, args.sweep_reps, os.path.join(PROFILES, "timing_all_workloads.md")))
         return
 

@@ -20,6 +20,8 @@ Workloads (B, H, N, d, storage dtype, causal):
   backward with grouped heads.
 * ``decode_gqa``           8, 32 query / 8 key-value heads, 1 query row against 8192 cached
   keys, 128, bf16, causal (the query is the newest position) -- forward only.
+* ``block_sparse_local``   1, 16, 16384, 128, bf16, no   -- forward + backward under the
+  local_global_block_mask pattern (9 of 128 key blocks per query block, about 7%).
 
 Recipe: each tensor is drawn i.i.d. N(0, 1) in fp32 on the CPU with
 ``torch.Generator().manual_seed(seed)`` and cast (round-to-nearest-even) to the storage
@@ -34,7 +36,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_cross_inputs", "torch_dtype", "elem_bytes", "fwd_flops", "bwd_flops"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_cross_inputs", "local_global_block_mask", "torch_dtype", "elem_bytes", "fwd_flops", "bwd_flops"]
 
 _DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -102,6 +104,7 @@ WORKLOADS = {
         Workload("smoke_2x4x512", 2, 4, 512, 64, "bf16", False, False, 0),
         Workload("gqa_causal_train", 1, 32, 8192, 128, "bf16", True, True, 6000, Hkv_=8),
         Workload("decode_gqa", 8, 32, 1, 128, "bf16", True, False, 7000, Hkv_=8, Nk_=8192),
+        Workload("block_sparse_local", 1, 16, 16384, 128, "bf16", False, True, 8000),
     ]
 }
 
@@ -146,6 +149,18 @@ def make_inputs(B: int, H: int, N: int, d: int, dtype: str, seed_base: int,
     if with_do:
         out["do"] = _randn(shape, seed_base + 4).to(td).contiguous()
     return out
+
+
+def local_global_block_mask(N: int, window: int = 4):
+    """uint8 (1, nb, nb) block mask (128 x 128 blocks, nb = ceil(N/128)): every query block
+    sees the key blocks within ``window`` of its own and the first key block -- a local
+    window plus one global block, the kind of fixed sparsity pattern block-sparse attention
+    serves."""
+    nb = -(-N // 128)
+    i = torch.arange(nb)[:, None]
+    j = torch.arange(nb)[None, :]
+    keep = ((i - j).abs() <= window) | (j == 0)
+    return keep.to(torch.uint8)[None].contiguous()
 
 
 def make_cross_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, dtype: str, seed_base: int,
