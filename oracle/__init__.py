@@ -28,6 +28,10 @@ Modules:
 * ``naive``     -- the definition written out: S = scale*Q K^T, P = softmax(S), O = P V,
                    per (batch, head), materialising S and P in fp64; the backward pass by
                    plain calculus of that definition (the pages give no gradient formulas).
+* ``fp8``       -- E4M3 quantization with block scales (the format decoded from its
+                   definition, nearest-even rounding, 128-row block and per-channel
+                   scales, a random rotation) and the FP8 kernel's tiled recurrence with
+                   P rounded to E4M3 ([FA-ch] FlashAttention-3, the FP8 lever).
 * ``tiled_ref`` -- the tiled online-softmax recurrence in the pages' order (query block
                    outer, key/value blocks inner, running max m, running sum l,
                    unnormalised o, one division at the end).  Used only to pin the
