@@ -255,6 +255,14 @@ def sweep(names, reps: int, out_path: str):
         if bm is not None:
             passes["fwd dense"] = lambda: fa.fa_forward(q, k, v, o, lse, causal=w.causal, stream=stream, split=ns,
                                                         workspace=wsf)
+        if name in ("large_head_causal", "long_bf16") and w.dtype == "bf16":
+            # the same workload through the E4M3 path (inputs quantized beforehand, not timed)
+            q8, qs8 = fa.fa_quantize_fp8(q)
+            k8, ks8 = fa.fa_quantize_fp8(k)
+            v8, vs8 = fa.fa_quantize_fp8(v, per_channel=True)
+            o8 = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+            passes["fwd fp8"] = lambda: fa.fa_forward_fp8(q8, qs8, k8, ks8, v8, vs8, o8, lse, causal=w.causal,
+                                                          stream=stream)
         if w.backward:
             do = inp["do"].to(dev)
             f32 = torch.float32
@@ -274,6 +282,7 @@ def sweep(names, reps: int, out_path: str):
                 "bwd": (5 * unit, qrows * (3 * w.d * s + 4 * w.d + 8) + kvrows * (2 * w.d * s + 8 * w.d)),
                 "3step": (2 * unit, qrows * (2 * w.d * s + 4) + kvrows * 2 * w.d * s)}
         info["fwd dense"], info["bwd dense"] = info["fwd"], info["bwd"]
+        info["fwd fp8"] = (info["fwd"][0], qrows * (d8 := w.d) + kvrows * 2 * d8 + qrows * (2 * d8 + 4))
         if w.N <= 16:
             # the plain three-step path for comparison: S = Q K^T, softmax, P V as library calls
             G = w.H // w.Hkv
@@ -327,7 +336,9 @@ def sweep(names, reps: int, out_path: str):
                 "512 MB fill between launches.  Shapes with a slash are query/key-value heads and query/key rows; "
                 "3step is the plain S = QK^T, softmax, PV path as three library calls (torch matmul and softmax), "
                 "timed for comparison on decode shapes.  block_sparse_local runs under its block mask (TFLOP/s "
-                "count the visible blocks only) and again dense for comparison.\n\n")
+                "count the visible blocks only) and again dense for comparison.  fwd fp8 is the same workload through "
+                "the E4M3 path (fa_forward_fp8 on inputs quantized beforehand); its % peak is against the bf16 "
+                "peak (the fp8 dense peak is twice that).\n\n")
         f.write("| workload | B x H x N x d | dtype | causal | pass | mode | median (us) | min (us) | TFLOP/s "
                 "| % peak | GB/s |\n|---|---|---|---|---|---|---|---|---|---|---|\n")
         for r in rows:

@@ -22,7 +22,7 @@ import os
 
 import torch  # the HIP runtime torch loads is the one libfa.so binds to (same soname)
 
-__all__ = ["MASK_BLOCK", "fa_forward", "fa_forward_split_count", "fa_backward", "fa_backward_dq", "fa_backward_dkdv", "fa_backward_workspace_bytes",
+__all__ = ["MASK_BLOCK", "fa_forward", "fa_forward_fp8", "fa_quantize_fp8", "fa_forward_split_count", "fa_backward", "fa_backward_dq", "fa_backward_dkdv", "fa_backward_workspace_bytes",
            "library", "FAError", "FA_F32", "FA_F16", "FA_BF16", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -79,6 +79,12 @@ def library() -> ctypes.CDLL:
     lib.fa_backward_sparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, i, vp, i, i,
                                        vp]
     lib.fa_backward_sparse.restype = i
+    lib.fa_fp8_scale_count.argtypes = [i, i, i, i, i]
+    lib.fa_fp8_scale_count.restype = sz
+    lib.fa_quantize_fp8.argtypes = [vp, vp, vp, i, i, i, i, i, i, vp]
+    lib.fa_quantize_fp8.restype = i
+    lib.fa_forward_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    lib.fa_forward_fp8.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -276,3 +282,41 @@ def fa_backward_dkdv(q, k, v, do, workspace, dk=None, dv=None, *, scale=None, ca
     _check(lib.fa_backward_dkdv_ex(*ptrs, workspace.numel() * workspace.element_size(), B, Hq, Hkv, Nq, Nk, d,
                                    ctypes.c_float(sc), int(bool(causal)), _DTYPE_CODE[dt], _stream(stream, q.device)))
     return dk, dv
+
+
+def fa_quantize_fp8(x, *, per_channel=False, stream=None):
+    """E4M3 codes (uint8, like x) and float32 scales of x (B, H, N, d): one scale per 128
+    rows of a head, or per channel of a head with per_channel=True."""
+    lib = library()
+    if x.dim() != 4:
+        raise ValueError("x must be (B, H, N, d)")
+    B, H, N, d = x.shape
+    if x.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    shape = (B, H, d) if per_channel else (B, H, (N + 127) // 128)
+    scales = torch.empty(shape, dtype=torch.float32, device=x.device)
+    _check(lib.fa_quantize_fp8(_gpu_tensor("x", x), _gpu_tensor("codes", codes), _gpu_tensor("scales", scales),
+                               B, H, N, d, int(bool(per_channel)), _DTYPE_CODE[x.dtype], _stream(stream, x.device)))
+    return codes, scales
+
+
+def fa_forward_fp8(q8, q_scale, k8, k_scale, v8, v_scale, o=None, lse=None, *, scale=None, causal=False,
+                   stream=None):
+    """O (bf16, like q8) and lse from E4M3 codes and their scales (see fa_quantize_fp8: row
+    blocks for q and k, channels for v)."""
+    lib = library()
+    B, Hq, Hkv, Nq, Nk, d = _shapes(q8, k8)
+    u8, f32 = torch.uint8, torch.float32
+    if o is None:
+        o = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=f32, device=q8.device)
+    ptrs = [_gpu_tensor("q8", q8, u8), _gpu_tensor("q_scale", q_scale, f32, (B, Hq, (Nq + 127) // 128)),
+            _gpu_tensor("k8", k8, u8), _gpu_tensor("k_scale", k_scale, f32, (B, Hkv, (Nk + 127) // 128)),
+            _gpu_tensor("v8", v8, u8, k8.shape), _gpu_tensor("v_scale", v_scale, f32, (B, Hkv, d)),
+            _gpu_tensor("o", o, torch.bfloat16, q8.shape), _gpu_tensor("lse", lse, f32, (B, Hq, Nq))]
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib.fa_forward_fp8(*ptrs, B, Hq, Hkv, Nq, Nk, d, ctypes.c_float(sc), int(bool(causal)),
+                              _stream(stream, q8.device)))
+    return o, lse

@@ -236,6 +236,39 @@ int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dO
                              stream);
 }
 
+size_t fa_fp8_scale_count(int B, int H, int N, int d, int per_channel) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
+  return per_channel ? (size_t)B * H * d : (size_t)B * H * ((N + 127) / 128);
+}
+
+int fa_quantize_fp8(const void* x, void* codes, float* scales, int B, int H, int N, int d, int per_channel,
+                    fa_dtype_t dtype, hipStream_t stream) {
+  if (!x || !codes || !scales) return FA_ERR_NULL;
+  int st = check_shape(B, H, H, N, N, d, (int)dtype, 0);
+  if (st != FA_OK) return st;
+  if (!aligned4(x) || !aligned16(codes) || !aligned16(scales)) return FA_ERR_ALIGN;
+  fa::QuantArgs a{x, (uint8_t*)codes, scales, B, H, N, d, per_channel != 0, (int)dtype, stream};
+  (void)hipGetLastError();
+  if (fa::launch_quantize_fp8(a) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+int fa_forward_fp8(const void* q8, const float* q_scale, const void* k8, const float* k_scale, const void* v8,
+                   const float* v_scale, void* o, float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                   float scale, int causal, hipStream_t stream) {
+  if (!q8 || !q_scale || !k8 || !k_scale || !v8 || !v_scale || !o || !lse) return FA_ERR_NULL;
+  int st = check_shape(B, Hq, Hkv, Nq, Nk, d, FA_BF16, causal);
+  if (st != FA_OK) return st;
+  if ((st = check_scale(scale)) != FA_OK) return st;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8) || !aligned16(o) || !aligned4(lse) || !aligned4(q_scale) ||
+      !aligned4(k_scale) || !aligned16(v_scale))
+    return FA_ERR_ALIGN;
+  fa::Fwd8Args a{q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal != 0, stream};
+  (void)hipGetLastError();
+  if (fa::launch_forward_fp8(a) != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";

@@ -1,0 +1,387 @@
+// FP8 (E4M3) attention forward on gfx950, and the quantizer that feeds it.
+//
+// Method ("Flash Attention", mlx.void.app, section FlashAttention-3, the FP8 lever): the
+// score and value products run on 8-bit E4M3 inputs (largest value 448), each small
+// block of Q and K carrying its own scale so that an outlier only coarsens its block.
+// Here Q and K have one scale per 128 rows of a head, V one scale per channel (applied
+// to O at the end), and the probabilities are rounded to E4M3 for the P V product.
+//
+// Mapping to CDNA4:
+//   * v_mfma_scale_f32_32x32x64_f8f6f4 with both operands E4M3 and unit block scales:
+//     64-deep contraction, 32 bytes per lane, twice the bf16 rate.  The hardware pairs
+//     byte j of lane l's A operand with byte j of the B operand's lane of the same half
+//     (l / 32); any key or channel order the two operands share gives the same product.
+//   * S^T = K Q^T as in the 16-bit kernel: K rows from LDS (two 16-byte reads per lane),
+//     Q rows in registers; the block scales fold into the exponent's multiplier.
+//   * O^T += V^T P^T: P^T is the S^T accumulator rounded to E4M3 and packed four keys per
+//     dword (v_cvt_pk_fp8_f32, nearest-even, no saturation needed: p <= 1).  V^T comes from
+//     the row-major V tile with ds_read_b64_tr_b8, each source lane pointing at the key
+//     row whose byte position matches the packed P.
+//   * The running max is updated at every 64-key tile (no lazy slack), so the rounding of
+//     P follows a fixed, reproducible rule.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kE4m3Max = 448.0f;
+constexpr int kScaleBlock = 128;  // rows per Q/K scale
+
+__device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  // operand formats 0 (E4M3) for A and B, E8M0 block scales 127 (= 1.0)
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+// two fp32 -> two E4M3 bytes in the low (HI = false) or high half of `w`
+template <bool HI>
+__device__ __forceinline__ int pack_fp8(float x, float y, int w) {
+  return __builtin_amdgcn_cvt_pk_fp8_f32(x, y, w, HI);
+}
+
+// ------------------------------------------------------------------------------------
+// Quantizer.  Rows mode: one workgroup per (head, 128-row block); scale = amax / 448 (1 if
+// the block is zero), codes = E4M3(x / scale).  Channel mode: scales per (head, channel)
+// over all rows, from a first pass of per-chunk maxima (atomic max on the float bits,
+// which order like unsigned integers for non-negative values), then the codes.
+// ------------------------------------------------------------------------------------
+template <class In>
+__device__ __forceinline__ float load_as_f32(const In* p, size_t i);
+template <>
+__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, size_t i) {
+  return __uint_as_float(((uint32_t)p[i]) << 16);  // bf16
+}
+template <>
+__device__ __forceinline__ float load_as_f32<float>(const float* p, size_t i) {
+  return p[i];
+}
+struct f16_in {
+  uint16_t u;
+};
+template <>
+__device__ __forceinline__ float load_as_f32<f16_in>(const f16_in* p, size_t i) {
+  return (float)__builtin_bit_cast(_Float16, p[i].u);
+}
+
+__device__ __forceinline__ uint8_t to_e4m3(float x) {
+  x = fminf(fmaxf(x, -kE4m3Max), kE4m3Max);
+  return (uint8_t)(pack_fp8<false>(x, 0.f, 0) & 0xff);
+}
+
+template <class In>
+__global__ __launch_bounds__(256) void quant_rows_kernel(const In* __restrict__ x, uint8_t* __restrict__ codes,
+                                                         float* __restrict__ scales, int N, int d) {
+  const int nb = (N + kScaleBlock - 1) / kScaleBlock;
+  const int bh = blockIdx.x / nb, blk = blockIdx.x % nb;
+  const int r0 = blk * kScaleBlock;
+  const int rows = min(kScaleBlock, N - r0);
+  const size_t base = ((size_t)bh * N + r0) * d;
+  const int count = rows * d;
+  __shared__ float red[4];
+  float amax = 0.f;
+  for (int i = threadIdx.x; i < count; i += 256) amax = fmaxf(amax, fabsf(load_as_f32(x, base + i)));
+  for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = amax > 0.f ? amax / kE4m3Max : 1.0f;
+  if (threadIdx.x == 0) scales[(size_t)bh * nb + blk] = s;
+  for (int i = threadIdx.x; i < count; i += 256) codes[base + i] = to_e4m3(load_as_f32(x, base + i) / s);
+}
+
+__global__ void fill_zero_kernel(uint32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+template <class In>
+__global__ __launch_bounds__(256) void channel_amax_kernel(const In* __restrict__ x, uint32_t* __restrict__ amax_bits,
+                                                           int N, int d, int rows_per_block) {
+  // grid: (heads, ceil(N / rows_per_block)); thread t handles channels t, t + 256, ...
+  const int bh = blockIdx.x, r0 = blockIdx.y * rows_per_block;
+  const int r1 = min(N, r0 + rows_per_block);
+  for (int c = threadIdx.x; c < d; c += 256) {
+    float m = 0.f;
+    for (int r = r0; r < r1; ++r) m = fmaxf(m, fabsf(load_as_f32(x, ((size_t)bh * N + r) * d + c)));
+    atomicMax(amax_bits + (size_t)bh * d + c, __float_as_uint(m));
+  }
+}
+
+template <class In>
+__global__ __launch_bounds__(256) void channel_quant_kernel(const In* __restrict__ x, uint8_t* __restrict__ codes,
+                                                            float* __restrict__ scales, int N, int d,
+                                                            size_t total) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int c = (int)(i % d);
+  const size_t bh = i / ((size_t)N * d);
+  codes[i] = to_e4m3(load_as_f32(x, i) / scales[bh * d + c]);
+}
+
+__global__ void channel_finish_kernel(float* __restrict__ scales, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) {
+    const float amax = scales[i];
+    scales[i] = amax > 0.f ? amax / kE4m3Max : 1.0f;
+  }
+}
+
+// ------------------------------------------------------------------------------------
+// Forward.  NW waves x 32 query rows, 64-key tiles of K and V (E4M3 bytes) double
+// buffered in LDS.
+// ------------------------------------------------------------------------------------
+struct Fwd8Params {
+  const uint8_t* Q;
+  const uint8_t* K;
+  const uint8_t* V;
+  const float* qs;  // (B*Hq, ceil(Nq/128))
+  const float* ks;  // (B*Hkv, ceil(Nk/128))
+  const float* vs;  // (B*Hkv, D)
+  uint16_t* O;      // bf16
+  float* LSE;
+  int BH, G, Nq, Nk;
+  float c;  // scale * log2(e)
+};
+
+// byte offset of 16-byte chunk `ch` of row r in a row-major tile of D bytes per row,
+// XOR-swizzled over the row's chunks
+template <int D>
+__device__ __forceinline__ int t8_off(int r, int ch) {
+  constexpr int CPR = D / 16;
+  return r * D + (((ch ^ (r % CPR)) & (CPR - 1)) << 4);
+}
+
+template <int D, int ROWS, int NT>
+__device__ __forceinline__ void tile8_load_async(FA_LDS uint8_t* tile, __amdgpu_buffer_rsrc_t rs, int row0, int tid) {
+  constexpr int CPR = D / 16;
+  constexpr int CHUNKS = ROWS * CPR;
+  constexpr int WAVES = NT / 64;
+  constexpr int NI = CHUNKS / 64;
+  static_assert(CHUNKS % 64 == 0 && NI % WAVES == 0, "tile split");
+  const int wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int t = 0; t < NI / WAVES; ++t) {
+    const int base = (t * WAVES + wave) * 64;  // LDS chunk index of lane 0
+    const int p = base + lane;
+    const int r = p / CPR, slot = p % CPR;
+    const int ch = (slot ^ (r % CPR)) & (CPR - 1);  // global chunk stored at this slot
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)(tile + base * 16), 16, (row0 + r) * D + (ch << 4), 0,
+                                             0, 0);
+  }
+}
+
+template <int D, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd8_kernel(const Fwd8Params P) {
+  constexpr int BC = 64;
+  constexpr int BR = 32 * NW;
+  constexpr int NT = NW * 64;
+  constexpr int TB = BC * D;  // bytes of one K or V tile
+  constexpr int DS = D / 64;  // 64-deep contraction steps over the head dimension
+  constexpr int DB = D / 32;
+  static_assert(kScaleBlock % BR == 0 && kScaleBlock % BC == 0, "scale blocks hold whole tiles");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TB];  // K0 K1 V0 V1
+  FA_LDS uint8_t* lds = (FA_LDS uint8_t*)smem;
+
+  const int Nq = P.Nq, Nk = P.Nk;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, c32 = lane & 31;
+  const int nqb = (Nq + BR - 1) / BR;
+  const int bh = blockIdx.x % P.BH;
+  int qb = blockIdx.x / P.BH;
+  if (CAUSAL) qb = nqb - 1 - qb;
+  const int q0 = qb * BR, qw0 = q0 + 32 * wave, qrow = qw0 + c32;
+  const int off = Nk - Nq;
+  const int kvh = bh / P.G;
+  const size_t head = (size_t)bh * Nq * D, kvhead = (size_t)kvh * Nk * D;
+  const auto rq = make_rsrc(P.Q + head, (uint32_t)Nq * D);
+  const auto rk = make_rsrc(P.K + kvhead, (uint32_t)Nk * D);
+  const auto rv = make_rsrc(P.V + kvhead, (uint32_t)Nk * D);
+  const int nkt_all = (Nk + BC - 1) / BC;
+  const int nkt = CAUSAL ? min(nkt_all, (q0 + BR - 1 + off) / BC + 1) : nkt_all;
+
+  tile8_load_async<D, BC, NT>(lds, rk, 0, tid);
+  tile8_load_async<D, BC, NT>(lds + 2 * TB, rv, 0, tid);
+
+  // this lane's query row: 32 bytes per contraction step (channels 64 st + 32 half + 0..31)
+  i32x8 qf[DS];
+#pragma unroll
+  for (int st = 0; st < DS; ++st) {
+    const u32x4 lo = buffer_load16(rq, qrow * D + 64 * st + 32 * half);
+    const u32x4 hi = buffer_load16(rq, qrow * D + 64 * st + 32 * half + 16);
+    qf[st] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+  const float sq = P.qs[(size_t)bh * ((Nq + kScaleBlock - 1) / kScaleBlock) + q0 / kScaleBlock];
+  const float* ksh = P.ks + (size_t)kvh * ((Nk + kScaleBlock - 1) / kScaleBlock);
+
+  // V^T operand: read r of 4 gives this lane the bytes of keys K(r, e, half), e = 0..7, at
+  // its channel; this lane serves as source (16-lane group g, index 2e + t) for the row
+  // K(r, e, g / 2) and the 8 channels 16 (g % 2) + 8 t of the 32-channel block
+  const int g = lane >> 4, src = lane & 15, e_src = src >> 1, t_src = src & 1;
+  auto key_of = [](int r, int e, int h) { return 32 * (r >> 1) + 16 * (r & 1) + 8 * (e >> 2) + 4 * h + (e & 3); };
+
+  float m = -INFINITY, l = 0.f;
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
+
+  for (int j = 0; j < nkt; ++j) {
+    wait_vmem();
+    __syncthreads();
+    const int cur = j & 1;
+    if (j + 1 < nkt) {
+      tile8_load_async<D, BC, NT>(lds + (cur ^ 1) * TB, rk, (j + 1) * BC, tid);
+      tile8_load_async<D, BC, NT>(lds + (2 + (cur ^ 1)) * TB, rv, (j + 1) * BC, tid);
+    }
+    const int k0 = j * BC;
+    if (CAUSAL && k0 > qw0 + 31 + off) continue;
+    const FA_LDS uint8_t* kt = lds + cur * TB;
+    const FA_LDS uint8_t* vt = lds + (2 + cur) * TB;
+
+    // S^T = K Q^T (unscaled codes), two 32-key blocks
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = (f32x16){};
+      const int r = 32 * kb + c32;
+#pragma unroll
+      for (int st = 0; st < DS; ++st) {
+        const u32x4 lo = *(const FA_LDS u32x4*)(kt + t8_off<D>(r, 4 * st + 2 * half));
+        const u32x4 hi = *(const FA_LDS u32x4*)(kt + t8_off<D>(r, 4 * st + 2 * half + 1));
+        const i32x8 a = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        s[kb] = mfma_fp8(a, qf[st], s[kb]);
+      }
+    }
+    const float cs = P.c * sq * ksh[k0 / kScaleBlock];  // exponent multiplier of this tile
+
+    if ((k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > qw0 + off)) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + 32 * kb + acc_row(i, half);
+          if (key >= Nk || (CAUSAL && key > qrow + off)) s[kb][i] = -INFINITY;
+        }
+    }
+    // running max over the tile (every tile), rescale, exponentials, E4M3 P
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mx = max_nan(max_nan(mx, s[kb][i]), s[kb][i + 1]);
+    mx = max_halves(mx) * cs;
+    const float m_new = fmaxf(m, mx);
+    const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - m_new);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] *= alpha;
+    const float mu = (m == -INFINITY) ? 0.f : m;
+    i32x8 p8;  // dword 4 kb + a: keys 32 kb + 8 a + 4 half + 0..3
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        float p[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          p[b] = fast_exp2(fmaf(s[kb][4 * a + b], cs, -mu));
+          rs += p[b];
+        }
+        int w = pack_fp8<false>(p[0], p[1], 0);
+        w = pack_fp8<true>(p[2], p[3], w);
+        p8[4 * kb + a] = w;
+      }
+    l += rs;
+
+    // O^T += V^T P^T, one MFMA per 32-channel block
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      i32x8 va;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = key_of(r, e_src, g >> 1);
+        const int ch = 32 * db + 16 * (g & 1) + 8 * t_src;  // this source's 8 channels
+        const int offb = t8_off<D>(key, ch >> 4) + (ch & 15);
+        const i32x2 w = __builtin_amdgcn_ds_read_tr8_b64_v2i32((FA_LDS i32x2*)(vt + offb));
+        va[2 * r] = w.x;
+        va[2 * r + 1] = w.y;
+      }
+      o[db] = mfma_fp8(va, p8, o[db]);
+    }
+  }
+
+  const float lt = sum_halves(l);
+  if (qrow >= Nq) return;
+  const float inv = 1.0f / lt;
+  const float* vsh = P.vs + (size_t)kvh * D;
+  uint16_t* orow = P.O + head + (size_t)qrow * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+      const int d = 32 * db + 8 * gg + 4 * half;
+      const f32x4 sv = *(const f32x4*)(vsh + d);
+      u32x2 w;
+      w.x = bf16_t::pack(o[db][4 * gg] * inv * sv.x, o[db][4 * gg + 1] * inv * sv.y);
+      w.y = bf16_t::pack(o[db][4 * gg + 2] * inv * sv.z, o[db][4 * gg + 3] * inv * sv.w);
+      *(u32x2*)(orow + d) = w;
+    }
+  if (half == 0) P.LSE[(size_t)bh * Nq + qrow] = (m + log2f(lt)) * kLn2;
+}
+
+// ------------------------------------------------------------------------------------
+// launchers
+// ------------------------------------------------------------------------------------
+namespace {
+constexpr int kNW8 = 4;
+
+template <int D, bool CAUSAL>
+hipError_t go8(const Fwd8Args& a) {
+  constexpr int BR = 32 * kNW8;
+  const int nqb = (a.Nq + BR - 1) / BR;
+  Fwd8Params p{(const uint8_t*)a.q, (const uint8_t*)a.k, (const uint8_t*)a.v, a.q_scale, a.k_scale, a.v_scale,
+               (uint16_t*)a.o, a.lse, a.B * a.Hq, a.Hq / a.Hkv, a.Nq, a.Nk, a.scale * kLog2e};
+  hipLaunchKernelGGL((fwd8_kernel<D, kNW8, CAUSAL>), dim3(a.B * a.Hq * nqb), dim3(kNW8 * 64), 0, a.stream, p);
+  return hipGetLastError();
+}
+
+template <class In>
+hipError_t quant(const QuantArgs& a) {
+  const In* x = (const In*)a.x;
+  const int heads = a.B * a.H;
+  if (!a.per_channel) {
+    const int nb = (a.N + kScaleBlock - 1) / kScaleBlock;
+    hipLaunchKernelGGL((quant_rows_kernel<In>), dim3(heads * nb), dim3(256), 0, a.stream, x, a.codes, a.scales, a.N,
+                       a.d);
+    return hipGetLastError();
+  }
+  const int ns = heads * a.d;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((ns + 255) / 256), dim3(256), 0, a.stream, (uint32_t*)a.scales, ns);
+  constexpr int kRows = 256;
+  hipLaunchKernelGGL((channel_amax_kernel<In>), dim3(heads, (a.N + kRows - 1) / kRows), dim3(256), 0, a.stream, x,
+                     (uint32_t*)a.scales, a.N, a.d, kRows);
+  hipLaunchKernelGGL(channel_finish_kernel, dim3((ns + 255) / 256), dim3(256), 0, a.stream, a.scales, ns);
+  const size_t total = (size_t)heads * a.N * a.d;
+  hipLaunchKernelGGL((channel_quant_kernel<In>), dim3((total + 255) / 256), dim3(256), 0, a.stream, x, a.codes,
+                     a.scales, a.N, a.d, total);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_forward_fp8(const Fwd8Args& a) {
+  if (a.d == 64) return a.causal ? go8<64, true>(a) : go8<64, false>(a);
+  return a.causal ? go8<128, true>(a) : go8<128, false>(a);
+}
+
+hipError_t launch_quantize_fp8(const QuantArgs& a) {
+  switch (a.dtype) {
+    case kDtypeBF16: return quant<uint16_t>(a);
+    case kDtypeF16: return quant<f16_in>(a);
+    case kDtypeF32: return quant<float>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -64,6 +64,35 @@ struct BwdArgs {
 constexpr int kStageDq = 1;    // dQ kernel (also writes D and lse*log2(e))
 constexpr int kStageDkdv = 2;  // dK/dV kernel (reads D and lse*log2(e))
 
+// FP8 forward: E4M3 codes with Q/K scales per 128 rows of a head and V scales per channel
+struct Fwd8Args {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* q_scale;  // (B*Hq, ceil(Nq/128))
+  const float* k_scale;  // (B*Hkv, ceil(Nk/128))
+  const float* v_scale;  // (B*Hkv, d)
+  void* o;               // bf16 (B, Hq, Nq, d)
+  float* lse;
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  bool causal;
+  hipStream_t stream;
+};
+
+struct QuantArgs {
+  const void* x;
+  uint8_t* codes;
+  float* scales;  // rows: (B*H, ceil(N/128)); per channel: (B*H, d)
+  int B, H, N, d;
+  bool per_channel;
+  int dtype;
+  hipStream_t stream;
+};
+
+hipError_t launch_forward_fp8(const Fwd8Args& a);
+hipError_t launch_quantize_fp8(const QuantArgs& a);
+
 hipError_t launch_forward(const FwdArgs& a);
 hipError_t launch_backward(const BwdArgs& a, int stages);
 

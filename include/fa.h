@@ -242,6 +242,44 @@ int fa_backward_sparse(const void* q, const void* k, const void* v, const void* 
                        const void* block_mask, int mask_heads,
                        fa_dtype_t dtype, hipStream_t stream);
 
+/*
+ * FP8 (E4M3) forward
+ * ------------------
+ * "Flash Attention" (mlx.void.app), section FlashAttention-3: fp8 products run at about
+ * twice the 16-bit rate; an E4M3 number has 256 bit patterns and a largest value of 448,
+ * so everything rests on the scale factors, and block quantization gives each block its
+ * own scale so that an outlier only coarsens its block.  Here:
+ *   fa_fp8_scale_count  floats of scales for x (B, H, N, d): B*H*ceil(N/128) per-row-block
+ *                       scales, or B*H*d per-channel scales (per_channel != 0); 0 on bad sizes.
+ *   fa_quantize_fp8     x (B, H, N, d) of `dtype` (fp32, fp16, bf16; 4-byte aligned) ->
+ *                       codes (uint8 E4M3 bit patterns, 16-byte aligned) and scales
+ *                       (float, 16-byte aligned): scale = max |x| / 448 over each 128-row
+ *                       block of a head (or each channel of a head), 1 for an all-zero block;
+ *                       code = E4M3(x / scale), nearest even, clamped to +-448.
+ *   fa_forward_fp8      O (bf16, like q) and lse (float) from codes q8 (B, Hq, Nq, d) with
+ *                       row-block scales (B*Hq, ceil(Nq/128)), k8 (B, Hkv, Nk, d) with
+ *                       row-block scales (B*Hkv, ceil(Nk/128)), and v8 (B, Hkv, Nk, d) with
+ *                       channel scales (B*Hkv, d), i.e. Q ~ code * q_scale of the row's block.
+ *                       The scores use the exact products of the codes (fp32 accumulation)
+ *                       times the two block scales; the probabilities (relative to the
+ *                       running max, updated every 64 keys) are summed in fp32 for the
+ *                       normaliser and lse, and rounded to E4M3 for the P V product; O is
+ *                       multiplied by the channel scales at the end.  Grouping, causal
+ *                       alignment and errors as for fa_forward_ex; d is 64 or 128.
+ * The error this adds over fp16 inputs is that of E4M3 rounding (see the tests' bounds);
+ * a fixed random rotation of Q and K before quantization (the page's incoherent
+ * processing) is the caller's choice and leaves the scores unchanged before rounding.
+ */
+size_t fa_fp8_scale_count(int B, int H, int N, int d, int per_channel);
+
+int fa_quantize_fp8(const void* x, void* codes, float* scales, int B, int H, int N, int d, int per_channel,
+                    fa_dtype_t dtype, hipStream_t stream);
+
+int fa_forward_fp8(const void* q8, const float* q_scale, const void* k8, const float* k_scale,
+                   const void* v8, const float* v_scale, void* o, float* lse,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                   hipStream_t stream);
+
 /* fa_status_string -- static, human-readable text for a status code. */
 const char* fa_status_string(int status);
 

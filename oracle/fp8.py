@@ -79,28 +79,30 @@ def e4m3_codes(x) -> np.ndarray:
     return torch.from_numpy(xc).to(torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(x.shape)
 
 
-def quantize_rows(x, block: int = BLOCK):
+def quantize_rows(x, block: int = BLOCK, dtype=np.float64):
     """x (B, H, N, d) -> (codes uint8 (B, H, N, d), scales (B, H, ceil(N/block))), with
-    x ~= decode(codes) * scale of the row's block."""
-    x = np.asarray(x, np.float64)
+    x ~= decode(codes) * scale of the row's block.  ``dtype`` is the precision of the
+    scale and of x / scale (np.float32 takes the rounding decisions as a GPU computing in
+    fp32 would)."""
+    x = np.asarray(x, dtype)
     B, H, N, d = x.shape
     nb = -(-N // block)
-    scales = np.ones((B, H, nb))
+    scales = np.ones((B, H, nb), dtype)
     codes = np.zeros(x.shape, np.uint8)
     for i in range(nb):
         blk = x[:, :, i * block:(i + 1) * block]
         amax = np.abs(blk).max(axis=(2, 3))
-        s = np.where(amax > 0, amax / E4M3_MAX, 1.0)
+        s = np.where(amax > 0, amax / dtype(E4M3_MAX), dtype(1.0)).astype(dtype)
         scales[:, :, i] = s
         codes[:, :, i * block:(i + 1) * block] = e4m3_codes(blk / s[:, :, None, None])
     return codes, scales
 
 
-def quantize_channels(x):
+def quantize_channels(x, dtype=np.float64):
     """x (B, H, N, d) -> (codes (B, H, N, d), scales (B, H, d)): one scale per channel."""
-    x = np.asarray(x, np.float64)
+    x = np.asarray(x, dtype)
     amax = np.abs(x).max(axis=2)
-    s = np.where(amax > 0, amax / E4M3_MAX, 1.0)
+    s = np.where(amax > 0, amax / dtype(E4M3_MAX), dtype(1.0)).astype(dtype)
     return e4m3_codes(x / s[:, :, None, :]), s
 
 
@@ -126,16 +128,30 @@ def rotation(d: int, seed: int = 0) -> np.ndarray:
     return (signs[:, None] * h) / math.sqrt(d)
 
 
-def tiled_forward_head(q, k, v, scale: float, causal: bool, bc: int = 64, round_p: bool = True):
+def near_tie(p, rel: float):
+    """(mask, step): where p >= 0 lies within rel * p of a midpoint between two E4M3 values
+    (so that a rounding of p computed with that much error may land on either), and the
+    grid step there."""
+    p = np.asarray(p, np.float64)
+    step = np.where(p >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(p, 2.0 ** -6))) - 3), 2.0 ** -9)
+    frac = p / step - np.floor(p / step)
+    return (np.abs(frac - 0.5) * step <= rel * p) & (p > 0), step
+
+
+def tiled_forward_head(q, k, v, scale: float, causal: bool, bc: int = 64, round_p: bool = True,
+                       tie_rel: float = 0.0):
     """One head of the FP8 kernel's recurrence on already-dequantized q (N_q, d), k, v
     (N_k, d); v here excludes its per-channel scale (the caller multiplies O by it).
-    Returns (O, lse)."""
+    Returns (O, lse), and with ``tie_rel`` > 0 also a (N_q, d) slack: how far O could move
+    if every probability within tie_rel (relative) of an E4M3 rounding midpoint rounded the
+    other way -- the room a computation whose exponentials carry that much error needs."""
     q, k, v = (np.asarray(a, np.float64) for a in (q, k, v))
     nq, nk = q.shape[0], k.shape[0]
     off = nk - nq
     m = np.full(nq, -np.inf)
     l = np.zeros(nq)
     o = np.zeros((nq, v.shape[1]))
+    slack = np.zeros((nq, v.shape[1]))
     rows = np.arange(nq)[:, None]
     for j0 in range(0, nk, bc):
         kj, vj = k[j0:j0 + bc], v[j0:j0 + bc]
@@ -150,16 +166,22 @@ def tiled_forward_head(q, k, v, scale: float, causal: bool, bc: int = 64, round_
         l = l * alpha + p.sum(axis=1)
         pr = e4m3_round(p) if round_p else p
         o = o * alpha[:, None] + pr @ vj
+        if tie_rel > 0:
+            amb, step = near_tie(p, tie_rel)
+            slack = slack * alpha[:, None] + (amb * step) @ np.abs(vj)
         m = m_new
+    if tie_rel > 0:
+        return o / l[:, None], m + np.log(l), slack / l[:, None]
     return o / l[:, None], m + np.log(l)
 
 
 def forward(q8, q_scale, k8, k_scale, v8, v_scale, scale: float, causal: bool, bc: int = 64, heads=None,
-            round_p: bool = True):
+            round_p: bool = True, tie_rel: float = 0.0):
     """FP8 forward over codes and scales: q8 (B, H_q, N_q, d) with (B, H_q, ceil(N_q/128))
     scales, k8 likewise over (B, H_kv, N_k, d), v8 (B, H_kv, N_k, d) with (B, H_kv, d)
     channel scales.  Query head h reads key/value head h // (H_q // H_kv).  Returns
-    (O, lse) float64; with ``heads`` only those (b, h) query heads (others NaN)."""
+    (O, lse) float64 (and the tie slack of ``tiled_forward_head``, scaled like O, when
+    ``tie_rel`` > 0); with ``heads`` only those (b, h) query heads (others NaN)."""
     qd = dequantize_rows(q8, q_scale)
     kd = dequantize_rows(k8, k_scale)
     vd = e4m3_decode()[np.asarray(v8)]
@@ -169,9 +191,14 @@ def forward(q8, q_scale, k8, k_scale, v8, v_scale, scale: float, causal: bool, b
     o = np.full(qd.shape, np.nan)
     lse = np.full((B, H, N), np.nan)
     todo = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    slack = np.full(qd.shape, np.nan)
     for b, h in todo:
         g = h // G
-        oh, lh = tiled_forward_head(qd[b, h], kd[b, g], vd[b, g], scale, causal, bc, round_p)
-        o[b, h] = oh * vs[b, g][None, :]
-        lse[b, h] = lh
+        res = tiled_forward_head(qd[b, h], kd[b, g], vd[b, g], scale, causal, bc, round_p, tie_rel)
+        o[b, h] = res[0] * vs[b, g][None, :]
+        lse[b, h] = res[1]
+        if tie_rel > 0:
+            slack[b, h] = res[2] * vs[b, g][None, :]
+    if tie_rel > 0:
+        return o, lse, slack
     return o, lse

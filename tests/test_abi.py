@@ -202,3 +202,22 @@ def test_sparse_entry_points_validate_before_launch():
     assert lib.fa_backward_sparse(*bargs, NUL, 1, fa.FA_BF16, NUL) == FA_ERR_NULL
     assert lib.fa_backward_sparse(*bargs, P, 2, fa.FA_BF16, NUL) == FA_ERR_SHAPE
     assert lib.fa_backward_sparse(*bargs, P, 1, fa.FA_F32, NUL) == FA_ERR_UNSUPPORTED
+
+
+@needs_lib
+def test_fp8_entry_points_validate_before_launch():
+    lib = fa.library()
+    assert lib.fa_fp8_scale_count(2, 3, 300, 64, 0) == 2 * 3 * 3
+    assert lib.fa_fp8_scale_count(2, 3, 300, 64, 1) == 2 * 3 * 64
+    assert lib.fa_fp8_scale_count(0, 3, 300, 64, 1) == 0
+    assert lib.fa_quantize_fp8(NUL, P, P2, 1, 1, 64, 64, 0, fa.FA_BF16, NUL) == FA_ERR_NULL
+    assert lib.fa_quantize_fp8(P, P, P2, 1, 1, 64, 96, 0, fa.FA_BF16, NUL) == FA_ERR_UNSUPPORTED
+    assert lib.fa_quantize_fp8(P, MIS, P2, 1, 1, 64, 64, 0, fa.FA_BF16, NUL) == FA_ERR_ALIGN
+    args = [P, P2, P, P2, P, P2, P2, P2]
+    assert lib.fa_forward_fp8(*args, 1, 4, 3, 64, 64, 128, ctypes.c_float(0.1), 0, NUL) == FA_ERR_SHAPE
+    assert lib.fa_forward_fp8(*args, 1, 4, 2, 65, 64, 128, ctypes.c_float(0.1), 1, NUL) == FA_ERR_SHAPE
+    assert lib.fa_forward_fp8(*args, 1, 4, 2, 64, 64, 96, ctypes.c_float(0.1), 0, NUL) == FA_ERR_UNSUPPORTED
+    assert lib.fa_forward_fp8(*args, 1, 4, 2, 64, 64, 128, ctypes.c_float(-1.0), 0, NUL) == FA_ERR_SCALE
+    bad = [P, P2, P, P2, P, MIS, P2, P2]
+    assert lib.fa_forward_fp8(*bad, 1, 4, 2, 64, 64, 128, ctypes.c_float(0.1), 0, NUL) == FA_ERR_ALIGN
+    assert lib.fa_forward_fp8(NUL, *args[1:], 1, 4, 2, 64, 64, 128, ctypes.c_float(0.1), 0, NUL) == FA_ERR_NULL

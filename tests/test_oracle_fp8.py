@@ -166,3 +166,31 @@ def test_fp8_mutants_are_caught():
     per_tensor = fp8.e4m3_codes(x / (amax / 448))
     c, _ = fp8.quantize_rows(x)
     assert (per_tensor[0, 0, 128:] != c[0, 0, 128:]).any()  # a per-tensor scale coarsens every block
+
+
+def test_near_tie_marks_midpoints():
+    t = fp8.e4m3_decode()
+    grid = np.unique(t[np.isfinite(t) & (t >= 0)])
+    mids = (grid[:-1] + grid[1:]) / 2
+    amb, step = fp8.near_tie(mids, 1e-9)
+    assert amb.all()
+    np.testing.assert_allclose(step, np.diff(grid), rtol=0, atol=0)
+    amb, _ = fp8.near_tie(grid[1:], 1e-3)                       # grid points are not ties
+    assert not amb.any()
+    amb, _ = fp8.near_tie(mids * (1 + 1e-4), 1e-5)
+    assert not amb.any()
+
+
+def test_tie_slack_bounds_a_perturbed_rounding():
+    """Perturbing every probability by at most 1e-6 (relative) before rounding moves O by
+    no more than the slack computed with tie_rel = 1e-6."""
+    r = np.random.default_rng(8)
+    q, k, v = (r.standard_normal((90, 8)) for _ in range(3))
+    o, lse, slack = fp8.tiled_forward_head(q, k, v, 0.5, True, 64, True, tie_rel=1e-6)
+    orig = fp8.e4m3_round
+    try:
+        fp8.e4m3_round = lambda x: orig(np.asarray(x) * (1 + 1e-6 * r.uniform(-1, 1, np.shape(x))))
+        o2, _ = fp8.tiled_forward_head(q, k, v, 0.5, True, 64, True)
+    finally:
+        fp8.e4m3_round = orig
+    assert (np.abs(o2 - o) <= slack + 1e-12).all()
