@@ -44,8 +44,8 @@ constexpr int kMaskBlock = 128;
 // ----------------------------------------------------------------------------------
 // 1. dQ (and D, lse2).  NW waves x 32 queries per workgroup; BC keys per tile.
 // ----------------------------------------------------------------------------------
-template <class T, int D, int NW, int BC, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_kernel(
+template <class T, int D, int NW, int BC, int WPE, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ delta,
     float* __restrict__ lse2, float* __restrict__ dQ, int BH, int G, int Nq, int Nk, float c, float scale,
@@ -204,8 +204,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // products run on the matrix core.  Per tile: barrier (Q, dO, statistics in LDS), A
 // computes and publishes P while B computes dP, barrier, both finish their products.
 // ----------------------------------------------------------------------------------
-template <class T, int D, int NP, int BQ, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_kernel(
+template <class T, int D, int NP, int BQ, int WPE, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ delta, const float* __restrict__ lse2,
     float* __restrict__ dK, float* __restrict__ dV, int BHkv, int G, int Nq, int Nk, float c, float scale,
@@ -398,6 +398,18 @@ constexpr int kNWq = 4, kBCq = 32;
 // 64 queries per streamed Q/dO tile: two accumulator blocks per wave between barriers
 constexpr int kBQkv = 64;
 
+// Waves per SIMD of the dQ and dK/dV kernels, per head dimension.  At d = 64 the
+// per-score VALU work weighs twice as much against the products as at d = 128, and the
+// kernels fit in fewer registers: three dQ waves (168 VGPRs) and four dK/dV waves (128
+// VGPRs, two workgroups per CU) hide it better than two (GPT-2-medium shape, causal
+// N = 1024: dQ 174 -> 148 us, dK/dV 211 -> 164 us).
+template <int D>
+struct BwdOcc;
+template <>
+struct BwdOcc<128> { static constexpr int Q = 2, KV = 2; };
+template <>
+struct BwdOcc<64> { static constexpr int Q = 3, KV = 4; };
+
 template <class T, int D, bool CAUSAL, bool SPARSE>
 hipError_t go(const BwdArgs& a, int stages) {
   const int nbq = (a.Nq + kMaskBlock - 1) / kMaskBlock, nbk = (a.Nk + kMaskBlock - 1) / kMaskBlock;
@@ -412,7 +424,7 @@ hipError_t go(const BwdArgs& a, int stages) {
   if (stages & kStageDq) {
     constexpr int BR = 32 * kNWq;
     const int nqb = (a.Nq + BR - 1) / BR;
-    hipLaunchKernelGGL((bwd_dq_kernel<T, D, kNWq, kBCq, CAUSAL, SPARSE>), dim3(BHq * nqb), dim3(kNWq * 64), 0,
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, kNWq, kBCq, BwdOcc<D>::Q, CAUSAL, SPARSE>), dim3(BHq * nqb), dim3(kNWq * 64), 0,
                        a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (const uint16_t*)a.dO, a.lse, delta, lse2, a.dq, BHq, G, a.Nq, a.Nk, c, a.scale, mask);
     hipError_t e = hipGetLastError();
@@ -421,7 +433,7 @@ hipError_t go(const BwdArgs& a, int stages) {
   if (stages & kStageDkdv) {
     constexpr int BKV = 32 * kNPkv;
     const int nkb = (a.Nk + BKV - 1) / BKV;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kNPkv, kBQkv, CAUSAL, SPARSE>), dim3(BHkv * nkb),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, kNPkv, kBQkv, BwdOcc<D>::KV, CAUSAL, SPARSE>), dim3(BHkv * nkb),
                        dim3(2 * kNPkv * 64), 0, a.stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (const uint16_t*)a.dO, delta, lse2, a.dk, a.dv, BHkv, G, a.Nq, a.Nk, c,
                        a.scale, mask);
