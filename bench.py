@@ -296,7 +296,7 @@ def sweep(names, reps: int, out_path: str):
                 p = torch.softmax(sm, dim=-1).to(q.dtype)
                 return torch.matmul(p, vc)
             passes["3step"] = three_step
-        small = 2 * (qrows + kvrows) * w.d * s < (128 << 20)
+        small = 2 * (qrows + kvrows) * w.d * s < (256 << 20)  # inputs and outputs fit the 256 MB MALL
         for pname, fn in passes.items():
             for mode in (["warm", "cold"] if small else ["warm"]):
                 for _ in range(10):
