@@ -12,8 +12,9 @@ Printed: one JSON line on stdout.  `value` is credited TFLOP/s of the whole step
 forward 4*B*H*N^2*d and backward 10*B*H*N^2*d (five N x N x d products including the
 recomputation of S), both halved for causal masking.  `roofline` describes the
 kernel with the largest share of the step's time: its algorithmic flops per launch
-over its average launch time, measured here with HIP events on the stream the
-kernels run on, against the MI355X dense bf16 MFMA peak (2516.6 TFLOP/s).
+(kernel_flops: the products that kernel needs on its own) over its average launch
+time, measured here with HIP events on the stream the kernels run on, against the
+MI355X dense bf16 MFMA peak (2516.6 TFLOP/s).
 `cpu_baseline` times the fp64 CPU oracle on a few heads of the same workload.
 """
 
@@ -227,9 +228,10 @@ def read_sclk():
 
 def sweep(names, reps: int, out_path: str):
     """Time fa_forward (and the backward stages) of each workload with HIP events on the
-    stream they run on: median and min over `reps` back-to-back launches ("warm": inputs
-    may sit in the 256 MB last-level cache) and, for workloads whose inputs fit in that
-    cache, again with a 512 MB fill between launches ("cold")."""
+    stream they run on: median and min over `reps` samples, each the mean of a burst of
+    back-to-back launches of at least about 1 ms ("warm": inputs may sit in the 256 MB
+    last-level cache) and, for workloads whose inputs fit in that cache, single launches
+    each after a 512 MB fill ("cold")."""
     import torch
     import exact_tiled_attention_forward_amd as fa
     from exact_tiled_attention_forward_amd.workloads import (WORKLOADS, elem_bytes, local_global_block_mask,
@@ -301,16 +303,29 @@ def sweep(names, reps: int, out_path: str):
             for mode in (["warm", "cold"] if small else ["warm"]):
                 for _ in range(10):
                     fn()
+                # warm: each sample times `burst` launches back to back (at least about 1 ms of
+                # work), so that host launch gaps do not count; cold: one launch right after the
+                # fill, which keeps the queue busy until the launch starts
+                burst = 1
+                if mode == "warm":
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    for _ in range(5):
+                        fn()
+                    b.record(stream)
+                    b.synchronize()
+                    burst = max(1, min(50, int(math.ceil(1.0 / (a.elapsed_time(b) / 5)))))
                 ts = []
                 for _ in range(reps):
                     if mode == "cold":
                         flush.fill_(1)
                     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     a.record(stream)
-                    fn()
+                    for _ in range(burst):
+                        fn()
                     b.record(stream)
                     b.synchronize()
-                    ts.append(a.elapsed_time(b))
+                    ts.append(a.elapsed_time(b) / burst)
                 ts.sort()
                 med, mn = ts[len(ts) // 2], ts[0]
                 flops, nbytes = info[pname]
@@ -332,8 +347,9 @@ def sweep(names, reps: int, out_path: str):
                 f"{sclk or 'not readable'}.\n")
         f.write("TFLOP/s use 4BHN^2d (forward) and 10BHN^2d (backward), halved when causal; % of the 2516.6 "
                 "TFLOP/s bf16/fp16 dense MFMA peak (fp32 rows: the same figure, for comparison only); GB/s are "
-                "algorithmic bytes (inputs read once, outputs written once) over the median time.  cold = a "
-                "512 MB fill between launches.  Shapes with a slash are query/key-value heads and query/key rows; "
+                "algorithmic bytes (inputs read once, outputs written once) over the median time.  warm = the mean "
+                "of a burst of back-to-back launches (at least about 1 ms of work per sample, so host launch "
+                "gaps do not count); cold = one launch right after a 512 MB fill.  Shapes with a slash are query/key-value heads and query/key rows; "
                 "3step is the plain S = QK^T, softmax, PV path as three library calls (torch matmul and softmax), "
                 "timed for comparison on decode shapes.  block_sparse_local runs under its block mask (TFLOP/s "
                 "count the visible blocks only) and again dense for comparison.  fwd fp8 is the same workload through "
@@ -348,12 +364,26 @@ def sweep(names, reps: int, out_path: str):
     return out_path
 
 
+def product_flops(w):
+    """Flops of one N x N x d product of the workload (half of it when causal)."""
+    return 2.0 * w.B * w.H * w.visible_pairs() * w.d
+
+
+def credited_flops(w):
+    """Credited flops of the step's passes: the forward's two products (S = QK^T, O = PV)
+    and the backward's five (S, dP = dO V^T, dV, dK, dQ)."""
+    unit = product_flops(w)
+    return {"fwd": 2 * unit, "bwd": 5 * unit}
+
+
 def kernel_flops(w):
-    """Credited (algorithmic) flops of each kernel per launch.  The forward kernel owns
-    S = QK^T and O = PV; of the backward's five products the dK/dV kernel owns S, dP,
-    dV and dK, the dQ kernel owns dQ."""
-    unit = 2.0 * w.B * w.H * w.visible_pairs() * w.d  # one N x N x d product (half of it when causal)
-    return {"fwd": 2 * unit, "bwd_dq": 1 * unit, "bwd_dkdv": 4 * unit}
+    """Algorithmic flops of each kernel per launch, as a kernel of its own: the forward
+    computes S and PV; the dQ kernel, which produces dQ from Q, K, V, dO and the logsumexp,
+    needs S, dP and dQ; the dK/dV kernel needs S, dP, dV and dK.  The two backward kernels
+    together count S and dP twice (the recomputation their split costs), so this per-kernel
+    figure feeds the roofline only; the step's value uses credited_flops."""
+    unit = product_flops(w)
+    return {"fwd": 2 * unit, "bwd_dq": 3 * unit, "bwd_dkdv": 4 * unit}
 
 
 def cpu_baseline(w, inp, heads: int):
@@ -485,7 +515,8 @@ def main():
     kernel_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, n in enumerate(names)}
 
     flops = kernel_flops(w)
-    step_flops = sum(flops[n] for n in names)
+    credited = credited_flops(w)
+    step_flops = credited["fwd"] + (credited["bwd"] if w.backward else 0.0)
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     dom = max(names, key=lambda n: kernel_ms[n])
     achieved = flops[dom] / (kernel_ms[dom] * 1e-3) / 1e12
@@ -522,7 +553,7 @@ def main():
     }
     if w.backward:
         bwd_ms = kernel_ms["bwd_dq"] + kernel_ms["bwd_dkdv"]
-        bwd_tf = (flops["bwd_dq"] + flops["bwd_dkdv"]) / (bwd_ms * 1e-3) / 1e12
+        bwd_tf = credited["bwd"] / (bwd_ms * 1e-3) / 1e12
         line["bwd_tflops"] = round(bwd_tf, 2)
         line["bwd_pct_of_peak"] = round(100 * bwd_tf / PEAK_BF16_TFLOPS, 2)
     log(f"{w.name}: step {ms_per_step:.3f} ms, {value:.1f} TFLOP/s; kernels (ms): "

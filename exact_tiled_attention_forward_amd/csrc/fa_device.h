@@ -175,9 +175,61 @@ __device__ __forceinline__ void tile_load_async(FA_LDS uint8_t* tile, __amdgpu_b
   }
 }
 
+// The same fill, with each 16-byte-per-lane load written as inline assembly, for kernels
+// that keep several tiles in flight.  The compiler treats an outstanding buffer_load ...
+// lds from its builtin as possibly writing whatever a later transposing LDS read
+// (ds_read_b64_tr_b16) reads, and waits for every outstanding load before such a read,
+// which would drain the whole ring of tiles on every tile.  Loads written as assembly
+// are invisible to that analysis, so the caller owns the ordering: it waits with
+// wait_vmem_upto for the loads of the tile it is about to read (they complete in issue
+// order) and then synchronises the workgroup.  rs is the buffer resource as four words
+// (rsrc_words), held in SGPRs.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is named as clobbered on purpose
+__device__ __forceinline__ void dma16(const FA_LDS void* lds_dst, const u32x4& rs, int voff) {
+  // wave-uniform LDS byte address, moved to an SGPR for the s_mov
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(rs)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int D, int ROWS, int NT>
+__device__ __forceinline__ void tile_load_async_asm(FA_LDS uint8_t* tile, const u32x4& rs, int row0, int tid) {
+  constexpr int CPR = D / 8;
+  constexpr int CHUNKS = ROWS * CPR;
+  constexpr int PER_INSTR = 64;
+  constexpr int WAVES = NT / 64;
+  constexpr int NI = CHUNKS / PER_INSTR;
+  static_assert(CHUNKS % PER_INSTR == 0 && (NI % WAVES == 0 || WAVES % NI == 0),
+                "tile must split evenly over waves");
+  const int wave = tid >> 6, lane = tid & 63;
+  auto issue = [&](int base) {
+    const int p = base + lane;
+    const int r = p / CPR;
+    const int c = (p % CPR) ^ swz<D>(r);
+    dma16(tile + base * 16, rs, (row0 + r) * (D * 2) + (c << 4));
+  };
+  if constexpr (NI % WAVES == 0) {
+#pragma unroll
+    for (int t = 0; t < NI / WAVES; ++t) issue((t * WAVES + wave) * PER_INSTR);
+  } else {
+    if (wave < NI) issue(wave * PER_INSTR);
+  }
+}
+
+// Buffer resource words of a raw (stride 0) buffer of `bytes` bytes at base.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return (u32x4){(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, kRsrcWord3};
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, (int)kRsrcWord3);
 }
+
 
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rs, int voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
@@ -187,6 +239,15 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t rs, int vo
 // asm: inline asm makes the compiler assume AGPRs may be in use and select the AGPR form of
 // every MFMA, which then costs a copy for each accumulator the VALU touches.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// s_waitcnt vmcnt(N): wait until at most N vector memory instructions of this wave are
+// outstanding (they complete in issue order).  vmcnt is 6 bits, split over bits 3:0 and
+// 15:14 of the immediate.
+template <int N>
+__device__ __forceinline__ void wait_vmem_upto() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // Value of x held by lane l^32 (the other half of the wave): v_permlane32_swap.
 __device__ __forceinline__ float other_half(float x) {

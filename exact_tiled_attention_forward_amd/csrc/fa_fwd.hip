@@ -366,6 +366,206 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 }
 
 // ----------------------------------------------------------------------------------
+// Few query rows: a key/value head whose group holds at most 32 packed rows (G * Nq <=
+// 32, e.g. a decode step).  The rows fill one 32-row block, so the 256-row kernel would
+// run every product of a tile on one wave.  Here the keys are spread over the waves
+// instead: tile t (64 keys) goes to the pair of waves 2 (t % 2), 2 (t % 2) + 1, one 32-key
+// half each.  Every wave keeps its own online-softmax state (m, l, lr, o) over the keys it
+// saw; at the end the four states are merged with the (m, l) rule of the tiled method
+// ("FlashAttention：IO 感知…", 基准/方法设计).  Tiles stream through a ring of four
+// K/V stages in LDS, so up to three tiles are in flight while one is in use: the work per
+// byte is small, and the kernel lives on how many bytes it keeps in flight.
+// ----------------------------------------------------------------------------------
+constexpr int kFewRows = 32;
+constexpr long kFewTarget = 256;  // workgroups the split count aims at: one per CU
+constexpr int kFewMinTiles = 4;
+
+template <class T, int D, bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(256) void fwd16_few_kernel(const Fwd16Params P) {
+  constexpr int NT = 256, BC = 64, ST = 4;
+  constexpr int TB = BC * D * 2;                 // bytes of one K or V tile
+  constexpr int LPT = 2 * (BC * D / 8) / NT;     // loads per wave per tile (K and V)
+  constexpr int DS = D / 16, DB = D / 32;
+  // ring stage s: K at 2s TB, V at (2s + 1) TB; then the 32 query rows
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * ST * TB + kFewRows * D * 2];
+  FA_LDS uint8_t* lds = (FA_LDS uint8_t*)(smem);
+  FA_LDS uint8_t* qt = lds + 2 * ST * TB;
+
+  const int Nq = P.Nq, Nk = P.Nk, R = P.G * P.Nq;
+  const float c = P.c;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, c32 = lane & 31;
+  const int bkv = blockIdx.x % P.BHkv;
+  const int split = blockIdx.x / P.BHkv;
+  const int qrow = c32;             // packed row of this lane (rows >= R read as zeros)
+  const int pos = qrow % Nq;
+  const int off = Nk - Nq;
+  int pmin, pmax;
+  pos_range(0, R - 1, Nq, pmin, pmax);
+  const int ntiles = block_key_tiles<kFewRows, BC, CAUSAL>(0, R, Nq, Nk);
+  const int j0 = SPLIT ? split * P.ct : 0;
+  const int j1 = SPLIT ? min(j0 + P.ct, ntiles) : ntiles;
+  if (j0 >= j1) return;  // an empty split: the merge does not read it
+  const int n = j1 - j0;
+
+  const size_t head = (size_t)bkv * R * D;
+  const size_t kvhead = (size_t)bkv * Nk * D;
+  const u32x4 rq = rsrc_words(P.Q + head, (uint32_t)R * D * 2);
+  const u32x4 rk = rsrc_words(P.K + kvhead, (uint32_t)Nk * D * 2);
+  const u32x4 rv = rsrc_words(P.V + kvhead, (uint32_t)Nk * D * 2);
+
+  // Every global load of the kernel goes through the ring's accounting: the query rows
+  // first, then up to ST - 1 tiles ahead.
+  tile_load_async_asm<D, kFewRows, NT>(qt, rq, 0, tid);
+  auto load = [&](int t) {  // tile t of the range into stage t % ST
+    FA_LDS uint8_t* st_ = lds + (t % ST) * 2 * TB;
+    tile_load_async_asm<D, BC, NT>(st_, rk, (j0 + t) * BC, tid);
+    tile_load_async_asm<D, BC, NT>(st_ + TB, rv, (j0 + t) * BC, tid);
+  };
+#pragma unroll
+  for (int t = 0; t < ST - 1; ++t)
+    if (t < n) load(t);
+  if (n >= ST - 1) wait_vmem_upto<(ST - 1) * LPT>();  // the query rows have landed
+  else if (n == 2) wait_vmem_upto<2 * LPT>();
+  else wait_vmem_upto<LPT>();
+  __syncthreads();
+  u32x4 qf[DS];
+#pragma unroll
+  for (int st = 0; st < DS; ++st) qf[st] = lds_row16<D>(qt, qrow, 2 * st + half);
+
+  const int kb = wave & 1;      // which 32-key half of a tile this wave takes
+  const int parity = wave >> 1; // which tiles: t % 2 == parity
+  float m = -INFINITY, l = 0.f, lr = 0.f;
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
+
+  for (int t = 0; t < n; ++t) {
+    // this wave's loads of tile t have landed once at most those of tiles t+1, t+2 remain
+    if (t + 2 < n) wait_vmem_upto<2 * LPT>();
+    else if (t + 1 < n) wait_vmem_upto<LPT>();
+    else wait_vmem_upto<0>();
+    __syncthreads();  // every wave's part of tile t is in LDS; stage (t - 1) % ST is free
+    if (t + ST - 1 < n) load(t + ST - 1);
+    if ((t & 1) != parity) continue;
+    const int k0 = (j0 + t) * BC + 32 * kb;  // this wave's 32 keys
+    if (CAUSAL && k0 > pmax + off) continue;  // no row sees them
+    const FA_LDS uint8_t* kt = lds + (t % ST) * 2 * TB;
+    const FA_LDS uint8_t* vt = kt + TB;
+
+    f32x16 s = (f32x16){};
+#pragma unroll
+    for (int st = 0; st < DS; ++st) s = T::mfma(lds_row16<D>(kt, 32 * kb + c32, 2 * st + half), qf[st], s);
+    if ((k0 + 32 > Nk) || (CAUSAL && k0 + 31 > pmin + off)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + acc_row(i, half);
+        s[i] = (key >= Nk || (CAUSAL && key > pos + off)) ? -INFINITY : s[i];
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) mx = max_nan(max_nan(mx, s[i]), s[i + 1]);
+    mx = max_halves(mx) * c;
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m - m_new);
+      l *= alpha;
+      lr *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      m = m_new;
+    }
+    const float mu = (m == -INFINITY) ? 0.f : m;
+    float rs = 0.f, rsr = 0.f;
+    uint32_t pk[8];
+#pragma unroll
+    for (int t2 = 0; t2 < 8; ++t2) {
+      const float p0 = fast_exp2(fmaf(s[2 * t2], c, -mu));
+      const float p1 = fast_exp2(fmaf(s[2 * t2 + 1], c, -mu));
+      rs += p0 + p1;
+      pk[t2] = T::pack(p0, p1);
+      rsr = T::sum2(pk[t2], rsr);
+    }
+    l += rs;
+    lr += rsr;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 b = (u32x4){pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]};
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] = T::mfma(lds_colop<D>(vt, 32 * kb + 16 * ks, 32 * db, lane), b, o[db]);
+    }
+  }
+
+  // merge the four waves' states: o [w][row][D], then m, l, lr [w][row]
+  const float lt = sum_halves(l), ltr = sum_halves(lr);
+  __syncthreads();  // every wave is done with the ring
+  float* xo = (float*)smem;
+  float* xm = xo + 4 * 32 * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * db + 8 * g + 4 * half;
+      *(f32x4*)(xo + (wave * 32 + c32) * D + d) = (f32x4){o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+    }
+  if (half == 0) {
+    xm[wave * 32 + c32] = m;
+    xm[128 + wave * 32 + c32] = lt;
+    xm[256 + wave * 32 + c32] = ltr;
+  }
+  __syncthreads();
+  // thread -> (row, 16 consecutive columns)
+  constexpr int CPT = D * 32 / NT;
+  const int r = tid / (D / CPT), d0 = (tid % (D / CPT)) * CPT;
+  if (r >= R) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, xm[w * 32 + r]);  // -inf only for a row that saw no key
+  float a[4], L = 0.f, LR = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float mw = xm[w * 32 + r];
+    a[w] = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+    L += a[w] * xm[128 + w * 32 + r];
+    LR += a[w] * xm[256 + w * 32 + r];
+  }
+  float acc[CPT];
+#pragma unroll
+  for (int e = 0; e < CPT; ++e) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) v += a[w] * xo[(w * 32 + r) * D + d0 + e];
+    acc[e] = v;
+  }
+  if (SPLIT) {
+    // partial result of this split, in the layout fwd_merge_kernel reads
+    const size_t nrows = (size_t)P.BHkv * R;
+    const size_t row = (size_t)split * nrows + (size_t)bkv * R + r;
+    float* prow = P.part + row * D + d0;
+#pragma unroll
+    for (int e = 0; e < CPT; e += 4) *(f32x4*)(prow + e) = (f32x4){acc[e], acc[e + 1], acc[e + 2], acc[e + 3]};
+    if (d0 == 0) {
+      float* pm = P.part + (size_t)P.nsplit * nrows * D;
+      pm[row] = M;
+      pm[(size_t)P.nsplit * nrows + row] = L;
+      pm[(size_t)2 * P.nsplit * nrows + row] = LR;
+    }
+    return;
+  }
+  const float inv = LR > 0.f ? 1.0f / LR : 0.f;
+  uint16_t* orow = P.O + head + (size_t)r * D + d0;
+#pragma unroll
+  for (int e = 0; e < CPT; e += 8) {
+    u32x4 w4;
+    w4.x = T::pack(acc[e] * inv, acc[e + 1] * inv);
+    w4.y = T::pack(acc[e + 2] * inv, acc[e + 3] * inv);
+    w4.z = T::pack(acc[e + 4] * inv, acc[e + 5] * inv);
+    w4.w = T::pack(acc[e + 6] * inv, acc[e + 7] * inv);
+    *(u32x4*)(orow + e) = w4;
+  }
+  if (d0 == 0) P.LSE[(size_t)bkv * R + r] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+}
+// ----------------------------------------------------------------------------------
 // fp32 inputs: the same schedule on v_mfma_f32_32x32x2_f32 (fp32 in, fp32 accumulate).
 // Tiles go through registers into padded LDS rows (K stride D+2, V stride D+8 floats),
 // which keeps both operand reads free of bank conflicts.
@@ -516,6 +716,32 @@ template <>
 struct Fwd16Shape<64> { static constexpr int NW = 8, BC = 64, WPE = 4; };
 constexpr int kNW32 = 2, kBC32 = 32;
 
+// A group of at most kFewRows packed rows: the key-parallel kernel, split over the key
+// range like the 256-row kernel and merged by the same merge kernel.
+template <class T, int D, bool CAUSAL>
+hipError_t go_few(const FwdArgs& a, Fwd16Params p) {
+  constexpr int BC = 64;
+  const int R = (a.Hq / a.Hkv) * a.Nq;
+  const int tiles = block_key_tiles<kFewRows, BC, CAUSAL>(0, R, a.Nq, a.Nk);
+  if (a.nsplit <= 1) {
+    p.ct = tiles;
+    hipLaunchKernelGGL((fwd16_few_kernel<T, D, CAUSAL, false>), dim3(p.BHkv), dim3(256), 0, a.stream, p);
+    return hipGetLastError();
+  }
+  p.ct = (tiles + a.nsplit - 1) / a.nsplit;
+  const int ns = (tiles + p.ct - 1) / p.ct;
+  p.nsplit = a.nsplit;
+  p.part = a.part;
+  hipLaunchKernelGGL((fwd16_few_kernel<T, D, CAUSAL, true>), dim3(p.BHkv * ns), dim3(256), 0, a.stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int NWM = 4;
+  const long nrows = (long)p.BHkv * R;
+  hipLaunchKernelGGL((fwd_merge_kernel<T, D, NWM, kFewRows, BC, CAUSAL>), dim3((nrows + NWM - 1) / NWM),
+                     dim3(NWM * 64), 0, a.stream, p);
+  return hipGetLastError();
+}
+
 template <class T, int D, bool CAUSAL, bool SPARSE>
 hipError_t go16(const FwdArgs& a) {
   using S = Fwd16Shape<D>;
@@ -527,6 +753,7 @@ hipError_t go16(const FwdArgs& a) {
   Fwd16Params p{(const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, (uint16_t*)a.o, a.lse,
                 BHkv, a.Hq / a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, 0, 1, nullptr,
                 a.bmask, a.Hkv, a.mask_heads == 1 ? 0 : nbq * nbk, nbk};
+  if (!SPARSE && R <= kFewRows) return go_few<T, D, CAUSAL>(a, p);
   if (a.nsplit <= 1) {
     p.ct = (a.Nk + S::BC - 1) / S::BC;
     hipLaunchKernelGGL((fwd16_kernel<T, D, S::NW, S::BC, S::WPE, CAUSAL, false, SPARSE>), dim3(BHkv * nqb),
@@ -597,6 +824,20 @@ int max_block_tiles(int R, int Nq, int Nk) {
 
 int fwd_suggest_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, bool causal, int dtype) {
   if (dtype == kDtypeF32) return 1;
+  if ((long)(Hq / Hkv) * Nq <= kFewRows) {
+    // key-parallel kernel: one workgroup per CU (128 KiB of LDS at d = 128), at least
+    // kFewMinTiles 64-key tiles per split so that the ring's fill and drain stay small
+    const int R = (Hq / Hkv) * Nq;
+    const int tiles = causal ? block_key_tiles<kFewRows, 64, true>(0, R, Nq, Nk)
+                             : block_key_tiles<kFewRows, 64, false>(0, R, Nq, Nk);
+    const long wg = (long)B * Hkv;
+    long want = (kFewTarget + wg - 1) / wg;
+    if (want > tiles / kFewMinTiles) want = tiles / kFewMinTiles;
+    if (want > 64) want = 64;
+    if (want < 2) return 1;
+    const int ct = (int)((tiles + want - 1) / want);
+    return (tiles + ct - 1) / ct;
+  }
   const int NW = d == 64 ? Fwd16Shape<64>::NW : Fwd16Shape<128>::NW;
   const int BR = 32 * NW;
   const long R = (long)(Hq / Hkv) * Nq;

@@ -193,9 +193,12 @@ int fa_backward_dkdv_ex(const void* q, const void* k, const void* v, const void*
  * them with the pages' (m, l) merge rule ("FlashAttention：IO 感知…", 基准/方法设计:
  * m = max(m1, m2), l = e^(m1-m) l1 + e^(m2-m) l2, and the same factors on o), which is
  * exact up to rounding order.  The rows of one key/value head's group are processed
- * together, so the group's K and V are read once per chunk.
+ * together, so the group's K and V are read once per chunk.  A group of at most 32 rows
+ * (G*Nq <= 32, a decode step) spreads each chunk's keys over the workgroup's waves
+ * instead of its rows, with three key tiles in flight.
  *   fa_forward_split_count    the split count the library suggests for these arguments
- *                             (1: the unsplit grid already gives each CU two workgroups).
+ *                             (1: the unsplit grid already gives each CU two workgroups;
+ *                             for groups of at most 32 rows, about one workgroup per CU).
  *   fa_forward_split_workspace_bytes
  *                             nsplit * B*Hq*Nq * (d + 3) * 4 bytes for nsplit >= 2 (0 for
  *                             nsplit < 2 or > 1024).
