@@ -159,16 +159,20 @@ __device__ __forceinline__ void tile8_load_async(FA_LDS uint8_t* tile, __amdgpu_
   constexpr int CHUNKS = ROWS * CPR;
   constexpr int WAVES = NT / 64;
   constexpr int NI = CHUNKS / 64;
-  static_assert(CHUNKS % 64 == 0 && NI % WAVES == 0, "tile split");
+  static_assert(CHUNKS % 64 == 0 && (NI % WAVES == 0 || WAVES % NI == 0), "tile split");
   const int wave = tid >> 6, lane = tid & 63;
-#pragma unroll
-  for (int t = 0; t < NI / WAVES; ++t) {
-    const int base = (t * WAVES + wave) * 64;  // LDS chunk index of lane 0
+  auto issue = [&](int base) {  // base: LDS chunk index of lane 0
     const int p = base + lane;
     const int r = p / CPR, slot = p % CPR;
     const int ch = (slot ^ (r % CPR)) & (CPR - 1);  // global chunk stored at this slot
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)(tile + base * 16), 16, (row0 + r) * D + (ch << 4), 0,
                                              0, 0);
+  };
+  if constexpr (NI % WAVES == 0) {
+#pragma unroll
+    for (int t = 0; t < NI / WAVES; ++t) issue((t * WAVES + wave) * 64);
+  } else {
+    if (wave < NI) issue(wave * 64);  // fewer instructions than waves: the first NI waves
   }
 }
 
@@ -180,7 +184,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   constexpr int TB = BC * D;  // bytes of one K or V tile
   constexpr int DS = D / 64;  // 64-deep contraction steps over the head dimension
   constexpr int DB = D / 32;
-  static_assert(kScaleBlock % BR == 0 && kScaleBlock % BC == 0, "scale blocks hold whole tiles");
+  static_assert(kScaleBlock % 32 == 0 && kScaleBlock % BC == 0, "scale blocks hold whole waves and tiles");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TB];  // K0 K1 V0 V1
   FA_LDS uint8_t* lds = (FA_LDS uint8_t*)smem;
 
@@ -211,7 +215,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const u32x4 hi = buffer_load16(rq, qrow * D + 64 * st + 32 * half + 16);
     qf[st] = (i32x8){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
-  const float sq = P.qs[(size_t)bh * ((Nq + kScaleBlock - 1) / kScaleBlock) + q0 / kScaleBlock];
+  const float sq = P.qs[(size_t)bh * ((Nq + kScaleBlock - 1) / kScaleBlock) + qw0 / kScaleBlock];  // this wave's block
   const float* ksh = P.ks + (size_t)kvh * ((Nk + kScaleBlock - 1) / kScaleBlock);
 
   // V^T operand: read r of 4 gives this lane the bytes of keys K(r, e, half), e = 0..7, at
@@ -335,7 +339,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // launchers
 // ------------------------------------------------------------------------------------
 namespace {
-constexpr int kNW8 = 4;
+constexpr int kNW8 = 4;  // 8 waves (256-row blocks) measured 10-20% slower
 
 template <int D, bool CAUSAL>
 hipError_t go8(const Fwd8Args& a) {

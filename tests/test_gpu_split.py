@@ -23,6 +23,11 @@ CASES = [
     (2, 2, 2, 300, 300, 128, "bf16", False, 7),
     (1, 2, 2, 64, 64, 64, "bf16", True, 1024),        # more splits than key tiles
     (1, 2, 1, 257, 1000, 64, "bf16", False, 2),
+    # groups of at most 32 packed rows run key-parallel; 33 rows go to the 256-row kernel
+    (1, 8, 1, 4, 1000, 128, "bf16", True, None),     # 8 x 4 = 32 rows, causal
+    (1, 8, 1, 4, 1000, 64, "f16", False, 3),         # 32 rows, forced split
+    (1, 3, 1, 11, 777, 128, "bf16", True, 2),        # 3 x 11 = 33 rows
+    (2, 4, 2, 1, 70, 128, "bf16", True, 1024),       # decode, more splits than key tiles
 ]
 
 
