@@ -103,3 +103,33 @@ def test_full_size_sampled_heads(name):
         ref = naive.backward_head(q[b, h], k[b, h], v[b, h], do[b, h], w.scale, w.causal)
         msg = check_grads(f"[{b},{h}]", tuple(g[b, h] for g in got), ref, w.dtype)
         print(f"{name} head ({b},{h}): {msg}")
+
+
+def test_values_beyond_fp16_range():
+    """bf16 inputs with one entry of 2^17 (beyond the fp16 range) in V, then in dO, then
+    none, through one workspace.  The large entry makes a few scores' dP, D and dS large
+    beside ordinary ones, so the hi + lo products must keep the small terms, and a call
+    after such inputs must not depend on what they left in the workspace.  The large
+    entry scales the gradients, so the bars scale with max|ref|."""
+    B, H, N, d, causal = 1, 2, 200, 64, True
+    ws = torch.empty(fa.fa_backward_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    for where in ("v", "do", None):
+        inp = make_inputs(B, H, N, d, "bf16", seed_base=9300, with_do=True)
+        if where == "v":
+            inp["v"][0, 1, 37, 5] = 2.0 ** 17
+        elif where == "do":
+            inp["do"][0, 0, 150, 3] = -(2.0 ** 17)
+        q, k, v, do = (inp[x].cuda() for x in ("q", "k", "v", "do"))
+        o, lse = fa.fa_forward(q, k, v, causal=causal)
+        got = fa.fa_backward(q, k, v, o, do, lse, causal=causal, workspace=ws)
+        torch.cuda.synchronize()
+        ref = naive.backward(*(to64(inp[x]) for x in ("q", "k", "v", "do")), 1 / math.sqrt(d), causal)
+        for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+            x = to64(g.cpu())
+            assert np.isfinite(x).all(), f"{where} {name}: non-finite gradient"
+            s = max(1.0, float(np.abs(r).max()))
+            e = np.abs(x - r)
+            print(f"large entry in {where}: {name} max {e.max():.2e} mean {e.mean():.2e} max|ref| {s:.2e}")
+            assert e.max() <= 1e-2 * s and e.mean() <= 1e-3 * s, f"{where} {name}"
+        if where is None:
+            check_grads("after the large entries", tuple(g.cpu() for g in got), ref, "bf16")
