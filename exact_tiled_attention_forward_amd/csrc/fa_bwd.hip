@@ -27,6 +27,8 @@
 //             holds K, computes S = Q K^T, P and dV^T += dO^T P; the other holds V,
 //             computes dP = dO V^T, dS and dK^T += Q^T dS (dO^T / Q^T from transposing
 //             LDS reads), with P handed over through LDS.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -59,7 +61,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TB];  // K0 K1 V0 V1
   FA_LDS uint8_t* lds = (FA_LDS uint8_t*)(smem);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, c32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), half = lane >> 5, c32 = lane & 31;
   const int nqb = (Nq + BR - 1) / BR;
   const int bh = blockIdx.x % BH;  // query head; it reads key/value head bh / G
   int qb = blockIdx.x / BH;
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(WPE
   FA_LDS uint8_t* lds = (FA_LDS uint8_t*)(smem);
   FA_LDS float* stats = (FA_LDS float*)(smem + 4 * TB);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, c32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), half = lane >> 5, c32 = lane & 31;
   const bool role_b = wave >= NP;
   const int pair = role_b ? wave - NP : wave;
   FA_LDS f32x4* pex = (FA_LDS f32x4*)(smem + 4 * TB + 2 * 2 * 64 * 4 + pair * PB);
@@ -316,7 +318,9 @@ __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(WPE
         for (int st = 0; st < DS; ++st)
           x[qb] = T::mfma(lds_row16<D>(role_b ? otile : qtile, 32 * qb + c32, 2 * st + half), kv[st], x[qb]);
       }
-      if (!role_b) {
+      // P = exp2(S c - lse2), in two versions behind a wave-uniform branch so that tiles
+      // off the diagonal and the ragged end skip the per-score mask arithmetic
+      auto probabilities = [&](auto masked) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
@@ -327,7 +331,7 @@ __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(WPE
             for (int e = 0; e < 4; ++e) {
               const int i = 4 * a + e;
               float p = fast_exp2(fmaf(x[qb][i], c, -lv[e]));
-              if (need_mask) {
+              if constexpr (decltype(masked)::value) {
                 const int q = q0 + r0 + e;
                 if (q >= Nq || (CAUSAL && krow > q + off)) p = 0.f;
               }
@@ -336,6 +340,10 @@ __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(WPE
             pex[(qb * 4 + a) * 64 + lane] = (f32x4){x[qb][4 * a], x[qb][4 * a + 1], x[qb][4 * a + 2], x[qb][4 * a + 3]};
           }
         }
+      };
+      if (!role_b) {
+        if (need_mask) probabilities(std::true_type{});
+        else probabilities(std::false_type{});
       }
     }
     __syncthreads();

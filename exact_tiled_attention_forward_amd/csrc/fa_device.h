@@ -146,6 +146,12 @@ __device__ __forceinline__ u32x4 lds_colop(const FA_LDS uint8_t* tile, int rbase
   return (u32x4){lo.x, lo.y, hi.x, hi.y};
 }
 
+// Index of the calling wave in its workgroup as a wave-uniform (scalar) value.  The
+// compiler does not infer that threadIdx.x / 64 is equal across a wave; conditions built
+// from the plain quotient then count as divergent and are exec-masked on every pass
+// instead of branched over.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
+
 // Fill `rows` x D tile (16-bit) from global rows [row0, row0 + rows) of a head whose
 // buffer resource covers exactly that head.  NT threads cooperate; each wave instruction
 // moves 1 KiB.  Out-of-range rows read as zeros.

@@ -189,7 +189,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   FA_LDS uint8_t* lds = (FA_LDS uint8_t*)smem;
 
   const int Nq = P.Nq, Nk = P.Nk;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, c32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), half = lane >> 5, c32 = lane & 31;
   const int nqb = (Nq + BR - 1) / BR;
   const int bh = blockIdx.x % P.BH;
   int qb = blockIdx.x / P.BH;

@@ -175,7 +175,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 
   const int Nq = P.Nq, Nk = P.Nk, R = P.G * P.Nq;
   const float c = P.c;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, c32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), half = lane >> 5, c32 = lane & 31;
   const int nqb = (R + BR - 1) / BR;
   const int bkv = blockIdx.x % P.BHkv;
   const int t = blockIdx.x / P.BHkv;
@@ -393,7 +393,7 @@ __global__ __launch_bounds__(256) void fwd16_few_kernel(const Fwd16Params P) {
 
   const int Nq = P.Nq, Nk = P.Nk, R = P.G * P.Nq;
   const float c = P.c;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, c32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), half = lane >> 5, c32 = lane & 31;
   const int bkv = blockIdx.x % P.BHkv;
   const int split = blockIdx.x / P.BHkv;
   const int qrow = c32;             // packed row of this lane (rows >= R read as zeros)
@@ -582,7 +582,7 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
   __shared__ __attribute__((aligned(16))) float ks_[BC * KS];
   __shared__ __attribute__((aligned(16))) float vs_[BC * VS];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5, c32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), half = lane >> 5, c32 = lane & 31;
   const int nqb = (Nq + BR - 1) / BR;
   const int bh = blockIdx.x % BH;
   int qb = blockIdx.x / BH;
