@@ -108,7 +108,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     return j;
   };
 
-  for (int pass = 0; pass < 2; ++pass) {
+  // the two passes as separate code (pass 0 sums D, pass 1 accumulates dQ), and the
+  // per-score step of each in a masked and an unmasked version behind a wave-uniform
+  // branch, so that no score pays for the other pass or for the mask test
+  auto run_pass = [&](auto pass_tag) {
+    constexpr int pass = decltype(pass_tag)::value;
     __syncthreads();  // the previous pass is done with both LDS buffers
     int j = next_tile(0);
     if (j < nkt) {
@@ -139,22 +143,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
           s = T::mfma(lds_row16<D>(kt, 32 * kb + c32, 2 * st + half), qf[st], s);
           dp = T::mfma(lds_row16<D>(vt, 32 * kb + c32, 2 * st + half), of[st], dp);
         }
+        auto scores = [&](auto masked) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = fast_exp2(fmaf(s[i], c, -l2));
-          if (need_mask) {
-            const int key = k0 + 32 * kb + acc_row(i, half);
-            if (key >= Nk || (CAUSAL && key > qrow + off)) p = 0.f;
+          for (int i = 0; i < 16; ++i) {
+            float p = fast_exp2(fmaf(s[i], c, -l2));
+            if constexpr (decltype(masked)::value) {
+              const int key = k0 + 32 * kb + acc_row(i, half);
+              if (key >= Nk || (CAUSAL && key > qrow + off)) p = 0.f;
+            }
+            if constexpr (pass == 0) dsum = fmaf(p, dp[i], dsum);
+            else dp[i] = p * (dp[i] - dl);
           }
-          if (pass == 0) dsum = fmaf(p, dp[i], dsum);
-          else dp[i] = p * (dp[i] - dl);
-        }
-        if (pass == 1) {
+        };
+        if (need_mask) scores(std::true_type{});
+        else scores(std::false_type{});
+        if constexpr (pass == 1) {
 #pragma unroll
           for (int t = 0; t < 8; ++t) split2<T>(dp[2 * t], dp[2 * t + 1], sh[kb][t], sl[kb][t]);
         }
       }
-      if (pass == 1) {
+      if constexpr (pass == 1) {
         // dQ^T += K^T (dS^T hi) + K^T (dS^T lo)
 #pragma unroll
         for (int ks = 0; ks < BC / 16; ++ks) {
@@ -170,14 +178,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         }
       }
     }
-    if (pass == 0) {
+    if constexpr (pass == 0) {
       dl = sum_halves(dsum);
       if (qvalid && half == 0) {
         delta[(size_t)bh * Nq + qrow] = dl;
         lse2[(size_t)bh * Nq + qrow] = l2;
       }
     }
-  }
+  };
+  run_pass(std::integral_constant<int, 0>{});
+  run_pass(std::integral_constant<int, 1>{});
 
   if (qvalid) {
     float* dqr = dQ + head + (size_t)qrow * D;
