@@ -321,6 +321,21 @@ __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(WPE
     // phase 1: A computes P and publishes it, B computes dP
     f32x16 x[QB];  // A: P, B: dP (rows = queries q0 + 32*qb + acc_row(i, half))
     if (active) {
+      // d = 128: A reads its 32 statistics before the score products, so that their LDS
+      // latency hides under the products, and stores P only after the last read (the
+      // compiler cannot tell the two LDS regions apart: a store between two reads would
+      // serialise each read behind the previous store).  At d = 64 (four waves per
+      // SIMD, 128 VGPRs) the 32 registers this holds would spill, so there the reads
+      // stay next to their use.
+      f32x4 lvh[QB][4];
+      if constexpr (D == 128) {
+        if (!role_b) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) lvh[qb][a] = *(const FA_LDS f32x4*)(l2 + 32 * qb + 8 * a + 4 * half);
+        }
+      }
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         x[qb] = (f32x16){};
@@ -331,23 +346,51 @@ __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(WPE
       // P = exp2(S c - lse2), in two versions behind a wave-uniform branch so that tiles
       // off the diagonal and the ragged end skip the per-score mask arithmetic
       auto probabilities = [&](auto masked) {
+        auto prob = [&](int qb, int a, const f32x4& lv) {
+          const int r0 = 32 * qb + 8 * a + 4 * half;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-#pragma unroll
-          for (int a = 0; a < 4; ++a) {
-            const int r0 = 32 * qb + 8 * a + 4 * half;
-            const f32x4 lv = *(const FA_LDS f32x4*)(l2 + r0);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int i = 4 * a + e;
-              float p = fast_exp2(fmaf(x[qb][i], c, -lv[e]));
-              if constexpr (decltype(masked)::value) {
-                const int q = q0 + r0 + e;
-                if (q >= Nq || (CAUSAL && krow > q + off)) p = 0.f;
-              }
-              x[qb][i] = p;
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * a + e;
+            float p = fast_exp2(fmaf(x[qb][i], c, -lv[e]));
+            if constexpr (decltype(masked)::value) {
+              const int q = q0 + r0 + e;
+              if (q >= Nq || (CAUSAL && krow > q + off)) p = 0.f;
             }
-            pex[(qb * 4 + a) * 64 + lane] = (f32x4){x[qb][4 * a], x[qb][4 * a + 1], x[qb][4 * a + 2], x[qb][4 * a + 3]};
+            x[qb][i] = p;
+          }
+        };
+        auto publish = [&](int qb, int a) {
+          pex[(qb * 4 + a) * 64 + lane] = (f32x4){x[qb][4 * a], x[qb][4 * a + 1], x[qb][4 * a + 2], x[qb][4 * a + 3]};
+        };
+        if constexpr (D == 128) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) prob(qb, a, lvh[qb][a]);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int a = 0; a < 4; ++a) publish(qb, a);
+        } else {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              const int r0 = 32 * qb + 8 * a + 4 * half;
+              const f32x4 lv = *(const FA_LDS f32x4*)(l2 + r0);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int i = 4 * a + e;
+                float p = fast_exp2(fmaf(x[qb][i], c, -lv[e]));
+                if constexpr (decltype(masked)::value) {
+                  const int q = q0 + r0 + e;
+                  if (q >= Nq || (CAUSAL && krow > q + off)) p = 0.f;
+                }
+                x[qb][i] = p;
+              }
+              pex[(qb * 4 + a) * 64 + lane] =
+                  (f32x4){x[qb][4 * a], x[qb][4 * a + 1], x[qb][4 * a + 2], x[qb][4 * a + 3]};
+            }
           }
         }
       };
