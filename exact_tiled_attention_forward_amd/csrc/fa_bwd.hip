@@ -403,9 +403,8 @@ __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(WPE
     if (!active) continue;
 
     // phase 2: A: dV^T += dO^T (P hi + P lo);  B: dS = P (dP - D), dK^T += Q^T (dS hi + dS lo)
-    uint32_t hi[QB][8], lo[QB][8];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+    const FA_LDS uint8_t* atile = role_b ? qtile : otile;  // Q^T for dK, dO^T for dV
+    auto split_block = [&](int qb, uint32_t* hi, uint32_t* lo) {
       if (role_b) {
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
@@ -417,19 +416,47 @@ __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(WPE
         }
       }
 #pragma unroll
-      for (int t = 0; t < 8; ++t) split2<T>(x[qb][2 * t], x[qb][2 * t + 1], hi[qb][t], lo[qb][t]);
-    }
-    const FA_LDS uint8_t* atile = role_b ? qtile : otile;  // Q^T for dK, dO^T for dV
+      for (int t = 0; t < 8; ++t) split2<T>(x[qb][2 * t], x[qb][2 * t + 1], hi[t], lo[t]);
+    };
+    auto products = [&](int qb, const uint32_t* hi, const uint32_t* lo) {
 #pragma unroll
-    for (int ks = 0; ks < BQ / 16; ++ks) {
-      const int qb = ks >> 1, mm = ks & 1;
-      const u32x4 bh_ = (u32x4){hi[qb][4 * mm], hi[qb][4 * mm + 1], hi[qb][4 * mm + 2], hi[qb][4 * mm + 3]};
-      const u32x4 bl_ = (u32x4){lo[qb][4 * mm], lo[qb][4 * mm + 1], lo[qb][4 * mm + 2], lo[qb][4 * mm + 3]};
+      for (int mm = 0; mm < 2; ++mm) {
+        const u32x4 bh_ = (u32x4){hi[4 * mm], hi[4 * mm + 1], hi[4 * mm + 2], hi[4 * mm + 3]};
+        const u32x4 bl_ = (u32x4){lo[4 * mm], lo[4 * mm + 1], lo[4 * mm + 2], lo[4 * mm + 3]};
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const u32x4 a = lds_colop<D>(atile, 16 * ks, 32 * db, lane);
-        acc[db] = T::mfma(a, bh_, acc[db]);
-        acc[db] = T::mfma(a, bl_, acc[db]);
+        for (int db = 0; db < DB; ++db) {
+          const u32x4 a = lds_colop<D>(atile, 32 * qb + 16 * mm, 32 * db, lane);
+          acc[db] = T::mfma(a, bh_, acc[db]);
+          acc[db] = T::mfma(a, bl_, acc[db]);
+        }
+      }
+    };
+    if constexpr (D == 128) {
+      // every block's split first, then all products: the compiler interleaves the
+      // products with the transposing reads best this way (3% faster than block by block)
+      uint32_t hi[QB][8], lo[QB][8];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) split_block(qb, hi[qb], lo[qb]);
+#pragma unroll
+      for (int ks = 0; ks < BQ / 16; ++ks) {
+        const int qb = ks >> 1, mm = ks & 1;
+        const u32x4 bh_ = (u32x4){hi[qb][4 * mm], hi[qb][4 * mm + 1], hi[qb][4 * mm + 2], hi[qb][4 * mm + 3]};
+        const u32x4 bl_ = (u32x4){lo[qb][4 * mm], lo[qb][4 * mm + 1], lo[qb][4 * mm + 2], lo[qb][4 * mm + 3]};
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const u32x4 a = lds_colop<D>(atile, 16 * ks, 32 * db, lane);
+          acc[db] = T::mfma(a, bh_, acc[db]);
+          acc[db] = T::mfma(a, bl_, acc[db]);
+        }
+      }
+    } else {
+      // block by block, so that only one block's pairs are live: at 128 VGPRs this
+      // halves the spilled registers and runs 4.5% faster
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        uint32_t hi[8], lo[8];
+        split_block(qb, hi, lo);
+        products(qb, hi, lo);
       }
     }
   }
