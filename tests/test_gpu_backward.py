@@ -30,7 +30,7 @@ def check_grads(tag, got, ref, dtype, floor_aware=False):
     return "; ".join(out)
 
 
-SMALL_N = [1, 2, 17, 64, 65, 127, 128, 129, 200, 300]
+SMALL_N = [1, 2, 17, 64, 65, 127, 128, 129, 200, 300, 511, 577]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])

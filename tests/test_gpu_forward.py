@@ -24,7 +24,7 @@ def run_fwd(inp, causal, scale=None):
     return o.cpu(), lse.cpu()
 
 
-SMALL_N = [1, 2, 3, 17, 63, 64, 65, 127, 128, 129, 255, 300]
+SMALL_N = [1, 2, 3, 17, 63, 64, 65, 127, 128, 129, 255, 300, 511, 577]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
