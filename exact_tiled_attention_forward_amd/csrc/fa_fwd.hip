@@ -847,6 +847,33 @@ int fwd_suggest_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, bool causa
   const int mt = d == 64 ? (causal ? max_block_tiles<64, true>((int)R, Nq, Nk) : max_block_tiles<64, false>((int)R, Nq, Nk))
                          : (causal ? max_block_tiles<128, true>((int)R, Nq, Nk)
                                    : max_block_tiles<128, false>((int)R, Nq, Nk));
+  if (causal) {
+    // Causal query blocks need fewer key tiles than the longest one, so a split count
+    // yields fewer than wg * nsplit working workgroups (splits past a block's last tile
+    // exit at once).  Take the most splits whose working workgroups stay within 9/10 of
+    // the target: each split adds merge work, and near the full target it costs more
+    // than the shorter chunks save (causal 8 x 4096 x 64 prefill: 4 splits 57.5 us with
+    // 320 working workgroups, 5: 54.2 with 392, 6: 53.2 with 456, 7: 56.1 with 488,
+    // 8: 59.0 with 576).
+    const int nqb = (int)((R + BR - 1) / BR);
+    auto working = [&](int ct) {
+      long n = 0;
+      for (int qb = 0; qb < nqb; ++qb) {
+        const int kt = d == 64 ? block_key_tiles<32 * Fwd16Shape<64>::NW, Fwd16Shape<64>::BC, true>(qb * BR, (int)R, Nq, Nk)
+                               : block_key_tiles<32 * Fwd16Shape<128>::NW, Fwd16Shape<128>::BC, true>(qb * BR, (int)R, Nq, Nk);
+        n += (kt + ct - 1) / ct;
+      }
+      return n * B * Hkv;
+    };
+    int best = 1;
+    for (int ns = 2; ns <= mt && ns <= 64; ++ns) {
+      const int ct = (mt + ns - 1) / ns;
+      if ((mt + ct - 1) / ct != ns) continue;  // the same chunks as a smaller count
+      if (working(ct) > kTarget * 9 / 10) break;
+      best = ns;
+    }
+    return best;
+  }
   long want = (kTarget + wg - 1) / wg;
   if (want > mt) want = mt;
   if (want > 64) want = 64;

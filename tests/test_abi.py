@@ -176,6 +176,11 @@ def test_split_entry_points_validate_before_launch():
     # a decode step (one query row per head) is split; a large grid is not
     assert lib.fa_forward_split_count(8, 32, 8, 1, 8192, 128, 1, fa.FA_BF16) > 1
     assert lib.fa_forward_split_count(2, 16, 16, 8192, 8192, 128, 1, fa.FA_BF16) == 1
+    # causal 8 x 4096 x 64 prefill: six splits leave 456 workgroups with tiles to process
+    # (seven would leave 488, past 9/10 of the 512 target); without the causal triangle
+    # every split works, and four reach the target
+    assert lib.fa_forward_split_count(1, 8, 8, 4096, 4096, 64, 1, fa.FA_BF16) == 6
+    assert lib.fa_forward_split_count(1, 8, 8, 4096, 4096, 64, 0, fa.FA_BF16) == 4
     assert lib.fa_forward_split_count(1, 1, 1, 256, 256, 64, 0, fa.FA_F32) == 1
     need = lib.fa_forward_split_workspace_bytes(1, 4, 1, 128, 4)
     args = (P, P, P, P2, P2, 1, 4, 2, 1, 512, 128, ctypes.c_float(0.125), 1)
