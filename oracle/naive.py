@@ -9,7 +9,7 @@ Definition ([FA-17] section 二, [FA-blog] section 1.1, [FA-ch] intro):
                                     [FA-ch] section 地基：流式 softmax)
     O = P V
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
 
 * causal: key j is visible to query i iff j <= i (lower triangle, diagonal
   included; [FA-17] section 四 and the mask remark in section 五, [FA-ch]
