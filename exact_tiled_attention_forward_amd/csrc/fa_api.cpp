@@ -41,6 +41,15 @@ int check_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d, int dtype, int ca
   return FA_OK;
 }
 
+// The 16-bit forward kernels address the G*Nq query rows of one key/value head's group
+// (G = Hq/Hkv consecutive query heads) through one buffer resource with 32-bit byte
+// offsets, so the packed group, G*Nq*d*2 bytes, must stay below 2^31.
+int check_group_rows(int Hq, int Hkv, int Nq, int d, int dtype) {
+  if (dtype == FA_F32) return FA_OK;  // the fp32 kernel addresses one head at a time
+  if ((int64_t)(Hq / Hkv) * Nq * d * elem_size(dtype) >= (int64_t)1 << 31) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
 int check_scale(float scale) {
   if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_SCALE;
   return FA_OK;
@@ -55,6 +64,7 @@ int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* l
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   int st = check_shape(B, Hq, Hkv, Nq, Nk, d, (int)dtype, causal);
   if (st != FA_OK) return st;
+  if ((st = check_group_rows(Hq, Hkv, Nq, d, (int)dtype)) != FA_OK) return st;
   if ((st = check_scale(scale)) != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse)) return FA_ERR_ALIGN;
 
@@ -83,6 +93,7 @@ int fa_forward_split(const void* q, const void* k, const void* v, void* o, float
   int st = check_shape(B, Hq, Hkv, Nq, Nk, d, (int)dtype, causal);
   if (st != FA_OK) return st;
   if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if ((st = check_group_rows(Hq, Hkv, Nq, d, (int)dtype)) != FA_OK) return st;
   // grid: every (key/value head, query block) times the splits
   if ((int64_t)B * Hq * ((Nq + 31) / 32 + 1) * nsplit >= (int64_t)1 << 31) return FA_ERR_SHAPE;
   if ((st = check_scale(scale)) != FA_OK) return st;
@@ -107,6 +118,7 @@ int fa_forward_sparse(const void* q, const void* k, const void* v, void* o, floa
   if (st != FA_OK) return st;
   if (mask_heads != 1 && mask_heads != Hq) return FA_ERR_SHAPE;
   if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
+  if ((st = check_group_rows(Hq, Hkv, Nq, d, (int)dtype)) != FA_OK) return st;
   if ((int64_t)B * Hq * ((Nq + 31) / 32 + 1) * nsplit >= (int64_t)1 << 31) return FA_ERR_SHAPE;
   if ((st = check_scale(scale)) != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse)) return FA_ERR_ALIGN;

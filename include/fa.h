@@ -73,8 +73,11 @@ typedef enum {
 
 /*
  * Largest N for head dimension d and element size s (bytes): one (b, h) slice of a
- * tensor, N*d*s bytes, must stay below 2^31 (the kernels address within a head with
- * 32-bit offsets).  B*H*ceil(N/32) must also fit a grid dimension.
+ * tensor, N*d*4 bytes (the fp32 gradients' size), must stay below 2^31 (the kernels
+ * address within a head with 32-bit offsets).  The 16-bit forward entry points also
+ * address the G*Nq query rows of a key/value head's group (G = Hq/Hkv) together, so
+ * G*Nq*d*2 must stay below 2^31 there.  Larger shapes return FA_ERR_SHAPE.
+ * B*H*ceil(N/32) must also fit a grid dimension.
  */
 
 /*

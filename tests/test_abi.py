@@ -145,6 +145,18 @@ def test_forward_ex_grouping_and_length_errors():
     assert fwd_ex(Nq=1, Nk=4096, causal=1) == FA_ERR_UNSUPPORTED
     assert fwd_ex(Nk=1 << 23, d=128, scale=-1.0) == FA_ERR_SHAPE  # a key head of 2^31 fp32 bytes
     assert fwd_ex(k=NUL) == FA_ERR_NULL
+    # 8 query heads sharing one key/value head at 2^21 rows, d = 128: each head fits 32-bit
+    # offsets (2^30 fp32 bytes) but the packed group the 16-bit forward addresses is 2^32
+    # bytes, which would wrap; it is rejected, also through the split and sparse entry points
+    big = dict(B=1, Hq=8, Hkv=1, Nq=1 << 21, Nk=1 << 21, d=128)
+    assert fwd_ex(**big) == FA_ERR_SHAPE
+    assert fwd_ex(**dict(big, Hq=4)) == FA_ERR_SHAPE            # 2^31 bytes: still too large
+    assert fwd_ex(**dict(big, Hq=2, scale=-1.0)) == FA_ERR_SCALE  # 2^30 bytes: the size passes
+    assert fwd_ex(**dict(big, dtype=fa.FA_F32, scale=-1.0)) == FA_ERR_SCALE  # fp32: one head at a time
+    lib = fa.library()
+    args = (P, P, P, P2, P2, 1, 8, 1, 1 << 21, 1 << 21, 128, ctypes.c_float(0.125), 0)
+    assert lib.fa_forward_split(*args, 2, P2, 1 << 40, fa.FA_BF16, NUL) == FA_ERR_SHAPE
+    assert lib.fa_forward_sparse(*args, P, 1, 1, NUL, 0, fa.FA_BF16, NUL) == FA_ERR_SHAPE
 
 
 @needs_lib
@@ -226,3 +238,4 @@ def test_fp8_entry_points_validate_before_launch():
     bad = [P, P2, P, P2, P, MIS, P2, P2]
     assert lib.fa_forward_fp8(*bad, 1, 4, 2, 64, 64, 128, ctypes.c_float(0.1), 0, NUL) == FA_ERR_ALIGN
     assert lib.fa_forward_fp8(NUL, *args[1:], 1, 4, 2, 64, 64, 128, ctypes.c_float(0.1), 0, NUL) == FA_ERR_NULL
+
