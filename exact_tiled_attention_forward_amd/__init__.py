@@ -198,6 +198,10 @@ def fa_forward(q, k, v, o=None, lse=None, *, scale=None, causal=False, stream=No
                                     int(bool(causal)), ns, pw, workspace.numel() * workspace.element_size(),
                                     _DTYPE_CODE[dt], _stream(stream, q.device)))
         return o, lse
+    if Hq == Hkv and Nq == Nk:  # the square entry point itself
+        _check(lib.fa_forward(pq, pk, pv, po, pl, B, Hq, Nq, d, ctypes.c_float(sc), int(bool(causal)),
+                              _DTYPE_CODE[dt], _stream(stream, q.device)))
+        return o, lse
     _check(lib.fa_forward_ex(pq, pk, pv, po, pl, B, Hq, Hkv, Nq, Nk, d, ctypes.c_float(sc), int(bool(causal)),
                              _DTYPE_CODE[dt], _stream(stream, q.device)))
     return o, lse
@@ -240,6 +244,10 @@ def fa_backward(q, k, v, o, do, lse, dq=None, dk=None, dv=None, *, scale=None, c
                                       ctypes.c_float(sc), int(bool(causal)), pm, mh, _DTYPE_CODE[dt],
                                       _stream(stream, q.device)))
         return dq, dk, dv
+    if Hq == Hkv and Nq == Nk:  # the square entry point itself
+        _check(lib.fa_backward(*ptrs, workspace.numel() * workspace.element_size(), B, Hq, Nq, d,
+                               ctypes.c_float(sc), int(bool(causal)), _DTYPE_CODE[dt], _stream(stream, q.device)))
+        return dq, dk, dv
     _check(lib.fa_backward_ex(*ptrs, workspace.numel() * workspace.element_size(), B, Hq, Hkv, Nq, Nk, d,
                               ctypes.c_float(sc), int(bool(causal)), _DTYPE_CODE[dt], _stream(stream, q.device)))
     return dq, dk, dv
@@ -259,6 +267,10 @@ def fa_backward_dq(q, k, v, do, lse, dq=None, *, scale=None, causal=False, works
             _gpu_tensor("do", do, dt, q.shape), _gpu_tensor("lse", lse, f32, (B, Hq, Nq)),
             _gpu_tensor("dq", dq, f32, q.shape), _gpu_tensor("workspace", workspace)]
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if Hq == Hkv and Nq == Nk:
+        _check(lib.fa_backward_dq(*ptrs, workspace.numel() * workspace.element_size(), B, Hq, Nq, d,
+                                  ctypes.c_float(sc), int(bool(causal)), _DTYPE_CODE[dt], _stream(stream, q.device)))
+        return dq, workspace
     _check(lib.fa_backward_dq_ex(*ptrs, workspace.numel() * workspace.element_size(), B, Hq, Hkv, Nq, Nk, d,
                                  ctypes.c_float(sc), int(bool(causal)), _DTYPE_CODE[dt], _stream(stream, q.device)))
     return dq, workspace
@@ -279,6 +291,10 @@ def fa_backward_dkdv(q, k, v, do, workspace, dk=None, dv=None, *, scale=None, ca
             _gpu_tensor("do", do, dt, q.shape), _gpu_tensor("dk", dk, f32, k.shape),
             _gpu_tensor("dv", dv, f32, k.shape), _gpu_tensor("workspace", workspace)]
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if Hq == Hkv and Nq == Nk:
+        _check(lib.fa_backward_dkdv(*ptrs, workspace.numel() * workspace.element_size(), B, Hq, Nq, d,
+                                    ctypes.c_float(sc), int(bool(causal)), _DTYPE_CODE[dt], _stream(stream, q.device)))
+        return dk, dv
     _check(lib.fa_backward_dkdv_ex(*ptrs, workspace.numel() * workspace.element_size(), B, Hq, Hkv, Nq, Nk, d,
                                    ctypes.c_float(sc), int(bool(causal)), _DTYPE_CODE[dt], _stream(stream, q.device)))
     return dk, dv

@@ -94,3 +94,72 @@ def assert_lse(lse, ref):
     assert np.isfinite(worst), "lse: non-finite values"
     assert worst <= LSE_REL, f"lse: relative err {worst:.3e} > {LSE_REL:.0e}"
     return worst
+
+
+class ErrorStats:
+    """Running error statistics of one output tensor over many heads: raw max and mean
+    |x - ref|, the output-rounding floor |round_out(ref) - ref| (max and mean), the largest
+    error beyond each element's own floor, and max |ref|.  For lse the error is the
+    relative one, |x - ref| / max(1, |ref|), and no floor applies."""
+
+    def __init__(self, out_dtype: str | None, relative: bool = False):
+        self.out_dtype, self.relative = out_dtype, relative
+        self.max = self.floor_max = self.excess_max = self.ref_max = 0.0
+        self.sum = self.floor_sum = 0.0
+        self.count = 0
+        self.nonfinite = 0
+
+    def add(self, x, ref):
+        x64, r64 = to64(x), to64(ref)
+        fin = np.isfinite(r64)
+        same_inf = ~fin & (x64 == r64)  # an empty row's lse = -inf on both sides
+        self.nonfinite += int((~np.isfinite(x64) & ~same_inf).sum())
+        x64, r64 = np.where(same_inf, 0.0, x64), np.where(same_inf, 0.0, r64)
+        d = np.abs(x64 - r64)
+        if self.relative:
+            d = d / np.maximum(1.0, np.abs(r64))
+            fl = np.zeros_like(d)
+        else:
+            fl = np.abs(_round_to(r64, self.out_dtype) - r64) if self.out_dtype else np.zeros_like(d)
+        self.max = max(self.max, float(d.max()))
+        self.sum += float(d.sum())
+        self.count += d.size
+        self.floor_max = max(self.floor_max, float(fl.max()))
+        self.floor_sum += float(fl.sum())
+        self.excess_max = max(self.excess_max, float((d - fl).max()))
+        self.ref_max = max(self.ref_max, float(np.abs(r64).max()))
+
+    def merge(self, other: "ErrorStats"):
+        self.max = max(self.max, other.max)
+        self.floor_max = max(self.floor_max, other.floor_max)
+        self.excess_max = max(self.excess_max, other.excess_max)
+        self.ref_max = max(self.ref_max, other.ref_max)
+        self.sum += other.sum
+        self.floor_sum += other.floor_sum
+        self.count += other.count
+        self.nonfinite += other.nonfinite
+
+    @property
+    def mean(self) -> float:
+        return self.sum / max(self.count, 1)
+
+    @property
+    def floor_mean(self) -> float:
+        return self.floor_sum / max(self.count, 1)
+
+    def as_dict(self):
+        return {"max": self.max, "mean": self.mean, "floor_max": self.floor_max, "floor_mean": self.floor_mean,
+                "beyond_floor_max": self.excess_max, "max_abs_ref": self.ref_max, "elements": self.count,
+                "nonfinite": self.nonfinite}
+
+    def check(self, name: str, bar_dtype: str):
+        """The bars of this module: lse relative <= LSE_REL; otherwise the max bar on the
+        error beyond the floor and the mean bar as written."""
+        assert self.nonfinite == 0, f"{name}: {self.nonfinite} non-finite values"
+        if self.relative:
+            assert self.max <= LSE_REL, f"{name}: relative err {self.max:.3e} > {LSE_REL:.0e}"
+            return
+        tmax, tmean = TOL[bar_dtype]["max"], TOL[bar_dtype]["mean"]
+        assert self.excess_max <= tmax, (f"{name}: error beyond the output rounding floor {self.excess_max:.3e} > "
+                                         f"{tmax:.0e} (raw max {self.max:.3e}, floor max {self.floor_max:.3e})")
+        assert self.mean <= tmean, f"{name}: mean abs err {self.mean:.3e} > {tmean:.0e} (max {self.max:.3e})"

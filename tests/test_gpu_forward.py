@@ -99,24 +99,3 @@ def test_smoke_shape_from_the_article():
     o_ref, lse_ref = naive.forward(to64(inp["q"]), to64(inp["k"]), to64(inp["v"]), w.scale, w.causal)
     assert_close("O", o, o_ref, w.dtype)
     assert_lse(lse, lse_ref)
-
-
-FULL = ["single_head_f32", "prefill_bf16", "gpt2_medium_train", "long_f16", "long_bf16", "large_head_causal"]
-
-
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_heads(name):
-    """The full workload in the launch configuration the benchmark times; every row of two
-    sampled heads (the first and the last) against the oracle."""
-    w = WORKLOADS[name]
-    inp = workload_inputs(w, with_do=False)
-    o, lse = run_fwd(inp, w.causal)
-    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
-    heads = sorted({(0, 0), (w.B - 1, w.H - 1)})
-    q, k, v = (to64(inp[x]) for x in ("q", "k", "v"))
-    for b, h in heads:
-        o_ref, lse_ref = naive.forward_head(q[b, h], k[b, h], v[b, h], w.scale, w.causal)
-        mx, mean, ex, fl = assert_close(f"O[{b},{h}]", o[b, h], o_ref, w.dtype)
-        worst = assert_lse(lse[b, h], lse_ref)
-        print(f"{name} head ({b},{h}): O max {mx:.3e} beyond-floor {ex:.3e} floor {fl:.3e} mean {mean:.3e} "
-              f"lse rel {worst:.2e}")
