@@ -194,3 +194,68 @@ def test_tie_slack_bounds_a_perturbed_rounding():
     finally:
         fp8.e4m3_round = orig
     assert (np.abs(o2 - o) <= slack + 1e-12).all()
+
+
+# Two rows whose exact E4M3 outcome follows from the format's grid by hand, and which
+# fix the model's schedule: keys in 64-key tiles aligned at key 0, the running max
+# updated at every tile, P rounded relative to it.  One query q = 1 (d = 1, scale 1),
+# key scores are the k values; "far" keys score -1000 (p = 0 exactly).
+A = math.log(0.515625)  # e^A = 0.515625 = 33/64, between the E4M3 values 0.5 and 0.5625
+
+
+def _row(nk, scores):
+    k = np.full((nk, 1), -1000.0)
+    v = np.zeros((nk, 2))
+    for j, (s, col) in scores.items():
+        k[j, 0] = s
+        v[j, col] = 1.0
+    return np.ones((1, 1)), k, v
+
+
+def test_schedule_pin_one_tile():
+    """Keys 0 (score A) and 40 (score 0) share the first 64-key tile: the tile max is 0, so
+    p_0 = 0.515625 is rounded to E4M3 before the P V product -> 0.5 (the nearer grid
+    value; the midpoint is 0.53125); the denominator uses the unrounded p.
+    O = (0.5, 1) / 1.515625, lse = ln 1.515625."""
+    q, k, v = _row(64, {0: (A, 0), 40: (0.0, 1)})
+    o, lse = fp8.tiled_forward_head(q, k, v, 1.0, False, bc=64, round_p=True)
+    np.testing.assert_allclose(o[0], [0.5 / 1.515625, 1 / 1.515625], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse[0], math.log(1.515625), rtol=0, atol=1e-15)
+
+
+def test_schedule_pin_two_tiles():
+    """Keys 0 (score A) and 64 (score 0) in consecutive tiles: tile 1 sees only key 0 (max A,
+    p_0 = 1, exact in E4M3), tile 2 raises the max to 0 and rescales o by e^A; p_64 = 1.
+    Nothing is rounded: O = (0.515625, 1) / 1.515625, the exact attention."""
+    q, k, v = _row(128, {0: (A, 0), 64: (0.0, 1)})
+    o, lse = fp8.tiled_forward_head(q, k, v, 1.0, False, bc=64, round_p=True)
+    np.testing.assert_allclose(o[0], [0.515625 / 1.515625, 1 / 1.515625], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse[0], math.log(1.515625), rtol=0, atol=1e-15)
+
+
+def test_schedule_pins_catch_other_schedules():
+    """A 32-key tiling puts keys 0 and 40 in different tiles (first pin fails: nothing is
+    rounded), and a lazily updated max (moved only when a tile's max exceeds it by 8 in
+    log2 units) keeps the reference at A in the second pin, so p_64 = 1/0.515625 = 1.939
+    is rounded to 2.0 (second pin fails)."""
+    q, k, v = _row(64, {0: (A, 0), 40: (0.0, 1)})
+    o32, _ = fp8.tiled_forward_head(q, k, v, 1.0, False, bc=32, round_p=True)
+    assert abs(o32[0, 0] - 0.5 / 1.515625) > 1e-3
+
+    def lazy(q, k, v, bc=64, slack=8.0):
+        m, l, o = -np.inf, 0.0, np.zeros(v.shape[1])
+        for j0 in range(0, k.shape[0], bc):
+            s = (q @ k[j0:j0 + bc].T)[0]
+            mx = s.max()
+            if mx * math.log2(math.e) > m * math.log2(math.e) + slack or m == -np.inf:
+                a = 0.0 if m == -np.inf else math.exp(m - mx)
+                l, o, m = l * a, o * a, max(m, mx)
+            p = np.exp(s - m)
+            l += p.sum()
+            o = o + fp8.e4m3_round(p) @ v[j0:j0 + bc]
+        return o / l
+
+    q, k, v = _row(128, {0: (A, 0), 64: (0.0, 1)})
+    ol = lazy(q, k, v)
+    np.testing.assert_allclose(ol, [1 / (1 + 1 / 0.515625), 2 / (1 + 1 / 0.515625)], rtol=0, atol=1e-12)
+    assert abs(ol[1] - 1 / 1.515625) > 1e-2
