@@ -22,7 +22,8 @@ import os
 
 import torch  # the HIP runtime torch loads is the one libfa.so binds to (same soname)
 
-__all__ = ["MASK_BLOCK", "fa_forward", "fa_forward_fp8", "fa_quantize_fp8", "fa_forward_split_count", "fa_backward", "fa_backward_dq", "fa_backward_dkdv", "fa_backward_workspace_bytes",
+__all__ = ["MASK_BLOCK", "fa_forward", "fa_forward_fp8", "fa_quantize_fp8", "fa_forward_split_count", "fa_backward", "fa_backward_dq", "fa_backward_dkdv", "fa_backward_noalloc",
+           "fa_backward_workspace_bytes",
            "library", "FAError", "FA_F32", "FA_F16", "FA_BF16", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
@@ -85,6 +86,8 @@ def library() -> ctypes.CDLL:
     lib.fa_quantize_fp8.restype = i
     lib.fa_forward_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     lib.fa_forward_fp8.restype = i
+    lib.fa_backward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+    lib.fa_backward_noalloc.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -250,6 +253,26 @@ def fa_backward(q, k, v, o, do, lse, dq=None, dk=None, dv=None, *, scale=None, c
         return dq, dk, dv
     _check(lib.fa_backward_ex(*ptrs, workspace.numel() * workspace.element_size(), B, Hq, Hkv, Nq, Nk, d,
                               ctypes.c_float(sc), int(bool(causal)), _DTYPE_CODE[dt], _stream(stream, q.device)))
+    return dq, dk, dv
+
+
+def fa_backward_noalloc(q, k, v, o, do, lse, dq, dk, dv, *, scale=None, causal=False, stream=None):
+    """fa_backward without a workspace: the row statistics live in the library's static
+    device scratch (at most 2^21 query rows B*Hq*Nq; see include/fa.h).  dq, dk, dv are
+    the caller's float32 outputs; nothing is allocated.  Calls that overlap in time on
+    one device race on the shared scratch."""
+    lib = library()
+    B, Hq, Hkv, Nq, Nk, d = _shapes(q, k)
+    dt, f32 = q.dtype, torch.float32
+    if dt not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {dt}")
+    ptrs = [_gpu_tensor("q", q, dt), _gpu_tensor("k", k, dt), _gpu_tensor("v", v, dt, k.shape),
+            _gpu_tensor("o", o, dt, q.shape), _gpu_tensor("do", do, dt, q.shape),
+            _gpu_tensor("lse", lse, f32, (B, Hq, Nq)), _gpu_tensor("dq", dq, f32, q.shape),
+            _gpu_tensor("dk", dk, f32, k.shape), _gpu_tensor("dv", dv, f32, k.shape)]
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    _check(lib.fa_backward_noalloc(*ptrs, B, Hq, Hkv, Nq, Nk, d, ctypes.c_float(sc), int(bool(causal)),
+                                   _DTYPE_CODE[dt], _stream(stream, q.device)))
     return dq, dk, dv
 
 

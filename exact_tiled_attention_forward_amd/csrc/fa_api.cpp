@@ -2,8 +2,12 @@
 // Every check runs before any HIP call, so a rejected call touches no device state.
 #include "fa.h"
 
+#include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+
+#include <atomic>
+#include <mutex>
 
 #include "fa_launch.h"
 
@@ -227,6 +231,75 @@ int fa_backward_sparse(const void* q, const void* k, const void* v, const void* 
                       fa::kStageDq | fa::kStageDkdv, block_mask, mask_heads);
 }
 
+}  // extern "C"
+
+// ----------------------------------------------------------------------------------
+// Backward without a caller workspace: the per-row statistics (D_i, lse_i*log2(e)) live in
+// a fixed device array of this library.  Each device holds its own copy of the array at
+// its own address, looked up once per device; kernels receive that address, never the
+// array's host-side name.
+// ----------------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on device `dev` (looked up with that device current the first
+// time, then cached); nullptr if the runtime refuses.
+void* scratch_on(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (p) return p;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+  void* addr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+  if (cur != dev) (void)hipSetDevice(cur);
+  if (e != hipSuccess || !addr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  g_scratch[dev].store(addr, std::memory_order_release);
+  return addr;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                        float* dq, float* dk, float* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                        int causal, fa_dtype_t dtype, hipStream_t stream) {
+  if (B < 1 || Hq < 1 || Nq < 1) return check_shape(B, Hq, Hkv, Nq, Nk, d, (int)dtype, causal);
+  const size_t need = fa_backward_workspace_bytes(B, Hq, Nq, d);
+  if (need > (size_t)FA_NOALLOC_SCRATCH_BYTES) {
+    // the other checks first, so that a call wrong in several ways reports the usual status
+    const int st = check_backward(q, k, v, o, dO, lse, dq, dk, dv, q, need, B, Hq, Hkv, Nq, Nk, d, scale, causal,
+                                  dtype);
+    return st != FA_OK ? st : FA_ERR_SCRATCH;
+  }
+  // every check but the workspace's, which the static array satisfies by construction
+  int st = check_backward(q, k, v, o, dO, lse, dq, dk, dv, q, need, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  int dev = -1;
+  if (stream) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return FA_ERR_HIP;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return FA_ERR_HIP;
+  }
+  void* ws = scratch_on(dev);
+  if (!ws) return FA_ERR_HIP;
+  return run_backward(q, k, v, dO, lse, dq, dk, dv, ws, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, stream,
+                      fa::kStageDq | fa::kStageDkdv);
+}
+
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
                 float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes, int B, int H, int N,
                 int d, float scale, int causal, fa_dtype_t dtype, hipStream_t stream) {
@@ -293,6 +366,9 @@ const char* fa_status_string(int status) {
     case FA_ERR_WORKSPACE: return "backward workspace is NULL or smaller than fa_backward_workspace_bytes()";
     case FA_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case FA_ERR_SCALE: return "scale must be finite and > 0";
+    case FA_ERR_SCRATCH:
+      return "fa_backward_noalloc: 8*B*Hq*Nq bytes of row statistics exceed its static scratch "
+             "(FA_NOALLOC_SCRATCH_BYTES); use fa_backward_ex with a caller workspace";
     default: return "unknown status";
   }
 }

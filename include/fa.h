@@ -68,7 +68,8 @@ typedef enum {
   FA_ERR_ALIGN = -4,       /* a tensor pointer is not 16-byte aligned */
   FA_ERR_WORKSPACE = -5,   /* backward workspace NULL or smaller than required */
   FA_ERR_HIP = -6,         /* the HIP runtime rejected a kernel launch */
-  FA_ERR_SCALE = -7        /* scale is not finite or not > 0 */
+  FA_ERR_SCALE = -7,       /* scale is not finite or not > 0 */
+  FA_ERR_SCRATCH = -8      /* fa_backward_noalloc: the call needs more than its static scratch */
 } fa_status_t;
 
 /*
@@ -285,6 +286,32 @@ int fa_forward_fp8(const void* q8, const float* q_scale, const void* k8, const f
                    const void* v8, const float* v_scale, void* o, float* lse,
                    int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                    hipStream_t stream);
+
+/*
+ * Backward for callers that cannot allocate
+ * -----------------------------------------
+ * For code under HIP graph capture, tight serving or training loops, and harnesses that
+ * forbid device allocation: fa_backward_noalloc is fa_backward_ex without the workspace
+ * argument.  The per-query-row statistics the two backward kernels exchange (D_i and
+ * lse_i*log2(e), 8 bytes per row) live in a static device array of the library,
+ * FA_NOALLOC_SCRATCH_BYTES (16 MiB) on every device the library runs on, held until the
+ * process ends.  That limits a call to B*Hq*Nq <= FA_NOALLOC_SCRATCH_BYTES / 8 = 2^21
+ * query rows (e.g. 2 x 16 x 8192 = 2^18); larger calls return FA_ERR_SCRATCH and enqueue
+ * nothing.  The call allocates no memory: on its first use on a device it looks up that
+ * device's copy of the array (with the stream's device current), then only launches the
+ * two kernels on `stream` (the null stream: the current device).  The array needs no
+ * clearing: the first kernel writes every row the second reads.  All calls on one device
+ * share its one array, so calls that overlap in time on one device (on different
+ * streams, or from several host threads without ordering) race and give wrong results;
+ * calls in stream order are safe.  Other arguments, results and errors as for
+ * fa_backward_ex (the same kernels; the results are bitwise equal).
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                        const float* lse, float* dq, float* dk, float* dv,
+                        int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                        fa_dtype_t dtype, hipStream_t stream);
 
 /* fa_status_string -- static, human-readable text for a status code. */
 const char* fa_status_string(int status);

@@ -16,6 +16,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_HIP, FA_ERR_SCALE = (
     0, -1, -2, -3, -4, -5, -6, -7)
+FA_ERR_SCRATCH = -8
 
 needs_lib = pytest.mark.skipif(not os.path.exists(fa.LIB_PATH), reason="libfa.so not built")
 
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_and_version():
     lib = fa.library()
     for st in (FA_OK, FA_ERR_NULL, FA_ERR_SHAPE, FA_ERR_UNSUPPORTED, FA_ERR_ALIGN, FA_ERR_WORKSPACE, FA_ERR_HIP,
-               FA_ERR_SCALE):
+               FA_ERR_SCALE, FA_ERR_SCRATCH):
         s = lib.fa_status_string(st).decode()
         assert s and s != "unknown status"
     assert lib.fa_status_string(12345).decode() == "unknown status"
@@ -239,3 +240,35 @@ def test_fp8_entry_points_validate_before_launch():
     assert lib.fa_forward_fp8(*bad, 1, 4, 2, 64, 64, 128, ctypes.c_float(0.1), 0, NUL) == FA_ERR_ALIGN
     assert lib.fa_forward_fp8(NUL, *args[1:], 1, 4, 2, 64, 64, 128, ctypes.c_float(0.1), 0, NUL) == FA_ERR_NULL
 
+
+@needs_lib
+def test_noalloc_backward_validates_before_launch():
+    """The workspace-free backward: the usual argument errors, and FA_ERR_SCRATCH for a call
+    whose 8 bytes per query row exceed the 16 MiB static scratch (2^21 rows), checked
+    before any device call."""
+    lib = fa.library()
+    f = ctypes.c_float(0.125)
+
+    def call(ptrs=None, B=1, Hq=4, Hkv=2, Nq=64, Nk=64, d=64, scale=f, causal=1, dtype=fa.FA_BF16):
+        ptrs = ptrs or [P] * 9
+        return lib.fa_backward_noalloc(*ptrs, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, NUL)
+
+    for i in range(9):
+        ptrs = [P] * 9
+        ptrs[i] = NUL
+        assert call(ptrs, d=96) == FA_ERR_NULL
+    assert call(d=96) == FA_ERR_UNSUPPORTED
+    assert call(dtype=fa.FA_F32) == FA_ERR_UNSUPPORTED
+    assert call(Hkv=3) == FA_ERR_SHAPE
+    assert call(Nq=0) == FA_ERR_SHAPE
+    assert call(Nq=65, causal=1) == FA_ERR_SHAPE
+    assert call(scale=ctypes.c_float(0.0)) == FA_ERR_SCALE
+    ptrs = [P] * 9
+    ptrs[7] = MIS
+    assert call(ptrs) == FA_ERR_ALIGN
+    # 2^21 + 1 query rows: one row over the static scratch
+    assert call(B=1, Hq=1, Hkv=1, Nq=(1 << 21) + 1, Nk=(1 << 21) + 1) == FA_ERR_SCRATCH
+    assert call(B=2, Hq=16, Hkv=16, Nq=(1 << 16) + 1, Nk=(1 << 16) + 1) == FA_ERR_SCRATCH
+    # a wrong argument is reported as such even when the call is also too large
+    assert call(B=2, Hq=16, Hkv=16, Nq=(1 << 16) + 1, Nk=(1 << 16) + 1, d=96) == FA_ERR_UNSUPPORTED
+    assert lib.fa_status_string(FA_ERR_SCRATCH).decode().startswith("fa_backward_noalloc")
