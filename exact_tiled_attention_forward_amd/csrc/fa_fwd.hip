@@ -46,6 +46,11 @@ namespace fa {
 // MFMAs run another wave's softmax runs on the VALU.
 // ----------------------------------------------------------------------------------
 constexpr float kRescaleSlack = 8.0f;
+// Largest sum of one lane's probabilities in a tile before the 256-row kernel at d = 64
+// moves its exponent reference: every probability then stays below 2^64, far from fp32
+// overflow.  Skipping the per-tile row max saves about a tenth of the softmax's vector
+// instructions (long non-causal d = 64 workload: 1.171 -> 1.127 ms).
+constexpr float kSumLimit = 18446744073709551616.0f;  // 2^64
 
 // Rows of the 16-bit kernel: the G*Nq query rows of one key/value head's group, packed.
 // The group's query heads are consecutive, so its rows are contiguous in Q and O, and
@@ -279,37 +284,85 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         }
     }
 
-    // online softmax: row max, lazy rescale, exponentials, sums, 16-bit P
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) mx = max_nan(max_nan(mx, s[kb][i]), s[kb][i + 1]);
-    mx = max_halves(mx) * c;
-    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m, mx);
-      const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m - m_new);  // o, l are 0 while m = -inf
-      l *= alpha;
-      lr *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) o[db] *= alpha;
-      m = m_new;
-    }
-    const float mu = (m == -INFINITY) ? 0.f : m;  // every score of such a row is -inf: p = 0
-    float rs = 0.f, rsr = 0.f;
+    // online softmax: exponentials, sums, 16-bit P
     uint32_t pk[KB][8];
+    if constexpr (D == 64 && !SPARSE) {
+      // The tile's row max is only taken when the exponent reference has to move: when
+      // some lane's sum of this tile's probabilities exceeds kSumLimit (or is not finite),
+      // which bounds every probability, or before the row's first visible key (m = -inf).
+      float rs, rsr;
+      auto exponentials = [&](float mu) {
+        rs = 0.f;
+        rsr = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int t2 = 0; t2 < 8; ++t2) {
-        const float p0 = fast_exp2(fmaf(s[kb][2 * t2], c, -mu));
-        const float p1 = fast_exp2(fmaf(s[kb][2 * t2 + 1], c, -mu));
-        rs += p0 + p1;
-        pk[kb][t2] = T::pack(p0, p1);
-        rsr = T::sum2(pk[kb][t2], rsr);
+          for (int t2 = 0; t2 < 8; ++t2) {
+            const float p0 = fast_exp2(fmaf(s[kb][2 * t2], c, -mu));
+            const float p1 = fast_exp2(fmaf(s[kb][2 * t2 + 1], c, -mu));
+            rs += p0 + p1;
+            pk[kb][t2] = T::pack(p0, p1);
+            rsr = T::sum2(pk[kb][t2], rsr);
+          }
+      };
+      bool move = __builtin_amdgcn_ballot_w64(m == -INFINITY) != 0;
+      if (!move) {
+        exponentials(m);
+        move = __builtin_amdgcn_ballot_w64(!(rs <= kSumLimit)) != 0;
       }
-    l += rs;
-    lr += rsr;
+      if (move) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) mx = max_nan(max_nan(mx, s[kb][i]), s[kb][i + 1]);
+        mx = max_halves(mx) * c;
+        const float m_new = fmaxf(m, mx);
+        const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m - m_new);  // o, l are 0 while m = -inf
+        l *= alpha;
+        lr *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        m = m_new;
+        exponentials(m == -INFINITY ? 0.f : m);  // every score of such a row is -inf: p = 0
+      }
+      l += rs;
+      lr += rsr;
+    } else {
+      // Row max every tile, and the lazy rule for the reference: the large-head
+      // workload's outlier rows would send many tiles through a second pass of
+      // exponentials under the sum check above (0.529 -> 0.559 ms).  Block-sparse
+      // launches keep it too (the sum check spills there).
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) mx = max_nan(max_nan(mx, s[kb][i]), s[kb][i + 1]);
+      mx = max_halves(mx) * c;
+      if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m, mx);
+        const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m - m_new);  // o, l are 0 while m = -inf
+        l *= alpha;
+        lr *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        m = m_new;
+      }
+      const float mu = (m == -INFINITY) ? 0.f : m;  // every score of such a row is -inf: p = 0
+      float rs = 0.f, rsr = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 8; ++t2) {
+          const float p0 = fast_exp2(fmaf(s[kb][2 * t2], c, -mu));
+          const float p1 = fast_exp2(fmaf(s[kb][2 * t2 + 1], c, -mu));
+          rs += p0 + p1;
+          pk[kb][t2] = T::pack(p0, p1);
+          rsr = T::sum2(pk[kb][t2], rsr);
+        }
+      l += rs;
+      lr += rsr;
+    }
 
     // O^T += V^T P^T
 #pragma unroll
