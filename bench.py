@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """One-GPU benchmark of exact tiled attention (forward + recompute backward) on MI355X.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload large_head_causal]
+    python bench.py [--gpus 1] [--steps 60] [--warmup 5] [--workload large_head_causal]
 
 A step is one pass of the whole path over the workload's synthetic inputs, already
 resident in HBM: fa_forward, then the two backward stages (fa_backward_dq,
@@ -234,7 +234,7 @@ def sweep(names, reps: int, out_path: str):
     each after a 512 MB fill ("cold")."""
     import torch
     import exact_tiled_attention_forward_amd as fa
-    from exact_tiled_attention_forward_amd.workloads import (WORKLOADS, elem_bytes, local_global_block_mask,
+    from exact_tiled_attention_forward_amd.workloads import (WORKLOADS, elem_bytes, workload_block_mask,
                                                              workload_inputs)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
@@ -251,7 +251,8 @@ def sweep(names, reps: int, out_path: str):
         if ns > 1:
             nbytes = fa.library().fa_forward_split_workspace_bytes(w.B, w.H, w.N, w.d, ns)
             wsf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        bm = local_global_block_mask(w.N).to(dev) if name == "block_sparse_local" else None
+        bm = workload_block_mask(w)
+        bm = bm.to(dev) if bm is not None else None
         passes = {"fwd": lambda: fa.fa_forward(q, k, v, o, lse, causal=w.causal, stream=stream, split=ns,
                                                workspace=wsf, block_mask=bm)}
         if bm is not None:
@@ -351,7 +352,7 @@ def sweep(names, reps: int, out_path: str):
                 "of a burst of back-to-back launches (at least about 1 ms of work per sample, so host launch "
                 "gaps do not count); cold = one launch right after a 512 MB fill.  Shapes with a slash are query/key-value heads and query/key rows; "
                 "3step is the plain S = QK^T, softmax, PV path as three library calls (torch matmul and softmax), "
-                "timed for comparison on decode shapes.  block_sparse_local runs under its block mask (TFLOP/s "
+                "timed for comparison on decode shapes.  block_sparse_local and block_sparse_butterfly run under their block masks (TFLOP/s "
                 "count the visible blocks only) and again dense for comparison.  fwd fp8 is the same workload through "
                 "the E4M3 path (fa_forward_fp8 on inputs quantized beforehand); its % peak is against the bf16 "
                 "peak (the fp8 dense peak is twice that).\n\n")
@@ -386,8 +387,32 @@ def kernel_flops(w):
     return {"fwd": 2 * unit, "bwd_dq": 3 * unit, "bwd_dkdv": 4 * unit}
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_vendor() -> str:
+    import numpy as np
+    try:
+        cfg = np.show_config(mode="dicts")
+        blas = cfg["Build Dependencies"]["blas"]
+        return f"{blas.get('name', '?')} {blas.get('version', '')}".strip()
+    except Exception:  # pragma: no cover - older numpy
+        return "unknown"
+
+
 def cpu_baseline(w, inp, heads: int):
-    """Time the fp64 oracle (forward + backward) on `heads` heads of the workload."""
+    """Time the fp64 oracle (forward, and backward where the workload has one) on `heads`
+    heads of the workload.  The oracle materialises the full N x N score matrix and skips
+    no masked work, so its rate is counted over the dense work it does: 4 N^2 d flop per
+    head for the forward and 10 N^2 d for the backward (not halved for causal masking)."""
     from oracle import naive
     try:
         import threadpoolctl
@@ -400,28 +425,32 @@ def cpu_baseline(w, inp, heads: int):
     arrs = {x: inp[x].double().numpy() for x in ("q", "k", "v", "do") if x in inp}
     t0 = time.perf_counter()
     for b, h in picks:
-        naive.forward_head(arrs["q"][b, h], arrs["k"][b, h], arrs["v"][b, h], w.scale, w.causal)
+        g = h // (w.H // w.Hkv)
+        naive.forward_head(arrs["q"][b, h], arrs["k"][b, g], arrs["v"][b, g], w.scale, w.causal)
         if w.backward:
-            naive.backward_head(arrs["q"][b, h], arrs["k"][b, h], arrs["v"][b, h], arrs["do"][b, h], w.scale,
+            naive.backward_head(arrs["q"][b, h], arrs["k"][b, g], arrs["v"][b, g], arrs["do"][b, h], w.scale,
                                 w.causal)
     secs = time.perf_counter() - t0
-    unit = 2.0 * w.N * w.N * w.d * (0.5 if w.causal else 1.0)  # one N x N x d product of one head
-    per_head = (2 + (5 if w.backward else 0)) * unit
+    dense_per_head = (4 + (10 if w.backward else 0)) * float(w.N) * w.Nk * w.d
     return {
-        "value": per_head * len(picks) / secs / 1e12,
+        "value": dense_per_head * len(picks) / secs / 1e12,
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
         "sample": f"{len(picks)} of {w.B * w.H} heads of {w.name}, fp64 numpy, "
-                  f"{'forward + backward' if w.backward else 'forward'}, {secs:.1f} s",
-        "seconds": secs,
+                  f"{'forward + backward' if w.backward else 'forward'}, {secs:.1f} s; rate over the oracle's "
+                  f"dense work ({4 + (10 if w.backward else 0)} N^2 d flop per head, not halved for causal)",
+        "seconds": round(secs, 3),
+        "cpu_model": _cpu_model(),
+        "blas": _blas_vendor(),
+        "heads_per_second": len(picks) / secs,
     }
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large_head_causal")
     ap.add_argument("--cpu-heads", type=int, default=12, help="heads of the CPU oracle sample (0: skip)")
@@ -461,7 +490,7 @@ def main():
 
     if args.sweep:
         names = ["single_head_f32", "prefill_bf16", "gpt2_medium_train", "long_f16", "long_bf16", "large_head_causal",
-                 "gqa_causal_train", "decode_gqa", "block_sparse_local"]
+                 "gqa_causal_train", "decode_gqa", "block_sparse_local", "block_sparse_butterfly"]
         log("wrote", sweep(names, args.sweep_reps, os.path.join(PROFILES, "timing_all_workloads.md")))
         return
 
@@ -513,6 +542,9 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
     kernel_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, n in enumerate(names)}
+    step_samples = sorted(e[0].elapsed_time(e[-1]) for e in evs)
+    kernel_samples = {n: sorted(e[j].elapsed_time(e[j + 1]) for e in evs) for j, n in enumerate(names)}
+    med = lambda v: v[len(v) // 2]  # noqa: E731
 
     flops = kernel_flops(w)
     credited = credited_flops(w)
@@ -540,7 +572,13 @@ def main():
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd_tflops": round(fwd_tf, 2),
         "fwd_pct_of_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2),
+        "ms_per_step_median": round(med(step_samples), 4),
+        "ms_per_step_min": round(step_samples[0], 4),
+        "timed_ms": round(total_ms, 2),
         "kernel_ms": {n: round(t, 4) for n, t in kernel_ms.items()},
+        "kernel_ms_median": {n: round(med(v), 4) for n, v in kernel_samples.items()},
+        "kernel_ms_min": {n: round(v[0], 4) for n, v in kernel_samples.items()},
+        "sclk": read_sclk(),
         "roofline": {
             "kernel": dom,
             "bound": "mfma",

@@ -22,6 +22,8 @@ Workloads (B, H, N, d, storage dtype, causal):
   keys, 128, bf16, causal (the query is the newest position) -- forward only.
 * ``block_sparse_local``   1, 16, 16384, 128, bf16, no   -- forward + backward under the
   local_global_block_mask pattern (9 of 128 key blocks per query block, about 7%).
+* ``block_sparse_butterfly`` 1, 16, 16384, 128, bf16, no -- forward + backward under the
+  butterfly_block_mask pattern (8 of 128 key blocks per query block, 6.25%).
 
 Recipe: each tensor is drawn i.i.d. N(0, 1) in fp32 on the CPU with
 ``torch.Generator().manual_seed(seed)`` and cast (round-to-nearest-even) to the storage
@@ -36,7 +38,8 @@ from dataclasses import dataclass, field
 
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_cross_inputs", "local_global_block_mask", "torch_dtype", "elem_bytes", "fwd_flops", "bwd_flops"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_cross_inputs", "local_global_block_mask",
+           "butterfly_block_mask", "workload_block_mask", "torch_dtype", "elem_bytes", "fwd_flops", "bwd_flops"]
 
 _DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -65,6 +68,7 @@ class Workload:
     note: str = field(default="", compare=False)
     Hkv_: int = 0  # key/value heads (0: H, one per query head)
     Nk_: int = 0   # key rows (0: N)
+    block_pattern: str = ""  # "" (dense), "local_global" or "butterfly" (128 x 128 block mask)
 
     @property
     def scale(self) -> float:
@@ -104,7 +108,8 @@ WORKLOADS = {
         Workload("smoke_2x4x512", 2, 4, 512, 64, "bf16", False, False, 0),
         Workload("gqa_causal_train", 1, 32, 8192, 128, "bf16", True, True, 6000, Hkv_=8),
         Workload("decode_gqa", 8, 32, 1, 128, "bf16", True, False, 7000, Hkv_=8, Nk_=8192),
-        Workload("block_sparse_local", 1, 16, 16384, 128, "bf16", False, True, 8000),
+        Workload("block_sparse_local", 1, 16, 16384, 128, "bf16", False, True, 8000, block_pattern="local_global"),
+        Workload("block_sparse_butterfly", 1, 16, 16384, 128, "bf16", False, True, 8100, block_pattern="butterfly"),
     ]
 }
 
@@ -161,6 +166,30 @@ def local_global_block_mask(N: int, window: int = 4):
     j = torch.arange(nb)[None, :]
     keep = ((i - j).abs() <= window) | (j == 0)
     return keep.to(torch.uint8)[None].contiguous()
+
+
+def butterfly_block_mask(N: int):
+    """uint8 (1, nb, nb) block mask (128 x 128 blocks, nb = ceil(N/128)) with the flat
+    butterfly pattern: query block i sees key block j iff i XOR j is 0 or a power of two,
+    i.e. the two block indices differ in at most one bit.  This is the union of the
+    supports of the log2(nb) butterfly factors (each pairs blocks whose indices differ in
+    one bit), so every block row holds 1 + log2(nb) visible blocks when nb is a power of
+    two: 8 of 128 (6.25%) at N = 16384."""
+    nb = -(-N // 128)
+    i = torch.arange(nb)[:, None]
+    j = torch.arange(nb)[None, :]
+    x = i ^ j
+    keep = (x & (x - 1)) == 0  # x == 0 or a power of two
+    return keep.to(torch.uint8)[None].contiguous()
+
+
+def workload_block_mask(w: "Workload"):
+    """The workload's block mask (CPU uint8 tensor), or None for a dense workload."""
+    if w.block_pattern == "local_global":
+        return local_global_block_mask(w.N)
+    if w.block_pattern == "butterfly":
+        return butterfly_block_mask(w.N)
+    return None
 
 
 def make_cross_inputs(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int, dtype: str, seed_base: int,

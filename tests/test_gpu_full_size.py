@@ -25,14 +25,14 @@ import pytest
 import torch
 
 import exact_tiled_attention_forward_amd as fa
-from exact_tiled_attention_forward_amd.workloads import WORKLOADS, local_global_block_mask, workload_inputs
+from exact_tiled_attention_forward_amd.workloads import WORKLOADS, workload_block_mask, workload_inputs
 from oracle import naive
 from parity import ErrorStats, to64
 
 pytestmark = pytest.mark.gpu
 
 FULL = ["single_head_f32", "prefill_bf16", "gpt2_medium_train", "long_f16", "long_bf16", "large_head_causal",
-        "smoke_2x4x512", "gqa_causal_train", "decode_gqa", "block_sparse_local"]
+        "smoke_2x4x512", "gqa_causal_train", "decode_gqa", "block_sparse_local", "block_sparse_butterfly"]
 
 HOST_BYTES = 64 << 30  # host memory the concurrent oracle heads may use together
 
@@ -72,7 +72,7 @@ def test_full_size_every_head(name):
     w = WORKLOADS[name]
     t0 = time.perf_counter()
     inp = workload_inputs(w)
-    bm = local_global_block_mask(w.N) if name == "block_sparse_local" else None
+    bm = workload_block_mask(w)
     got, ns = _gpu(w, inp, bm)
     t_gpu = time.perf_counter() - t0
     q, k, v = (inp[x] for x in ("q", "k", "v"))

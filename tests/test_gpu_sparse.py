@@ -82,3 +82,26 @@ def test_all_ones_mask_equals_dense():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_butterfly_mask_forward_and_backward(causal):
+    """The flat butterfly block pattern (block i sees block j iff i XOR j is 0 or a power
+    of two) at a ragged length, grouped heads, one mask layer for every head."""
+    from exact_tiled_attention_forward_amd.workloads import butterfly_block_mask
+    B, Hq, Hkv, N, d = 1, 4, 2, 1000, 128
+    bm = butterfly_block_mask(N)
+    assert bm.shape == (1, 8, 8) and int(bm[0].sum(1).min()) == 4
+    inp = make_cross_inputs(B, Hq, Hkv, N, N, d, "bf16", seed_base=13700, with_do=True)
+    q, k, v, do = (inp[x].cuda() for x in ("q", "k", "v", "do"))
+    bmg = bm.cuda()
+    o, lse = fa.fa_forward(q, k, v, causal=causal, block_mask=bmg)
+    dq, dk, dv = fa.fa_backward(q, k, v, o, do, lse, causal=causal, block_mask=bmg)
+    torch.cuda.synchronize()
+    ref_in = [to64(inp[x]) for x in ("q", "k", "v")]
+    o_ref, lse_ref = naive.forward(*ref_in, 1 / math.sqrt(d), causal, block_mask=bm.numpy())
+    assert_close("butterfly O", o.cpu(), o_ref, "bf16")
+    check_lse(lse.cpu(), lse_ref)
+    ref = naive.backward(*ref_in, to64(inp["do"]), 1 / math.sqrt(d), causal, block_mask=bm.numpy())
+    for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), ref):
+        assert_close(f"butterfly {name}", g.cpu(), r, "bf16", out_dtype="f32")
