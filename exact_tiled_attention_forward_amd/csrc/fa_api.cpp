@@ -96,7 +96,6 @@ int fa_forward_split(const void* q, const void* k, const void* v, void* o, float
   if (nsplit < 1 || nsplit > kMaxSplits) return FA_ERR_SHAPE;
   int st = check_shape(B, Hq, Hkv, Nq, Nk, d, (int)dtype, causal);
   if (st != FA_OK) return st;
-  if (dtype == FA_F32) return FA_ERR_UNSUPPORTED;
   if ((st = check_group_rows(Hq, Hkv, Nq, d, (int)dtype)) != FA_OK) return st;
   // grid: every (key/value head, query block) times the splits
   if ((int64_t)B * Hq * ((Nq + 31) / 32 + 1) * nsplit >= (int64_t)1 << 31) return FA_ERR_SHAPE;

@@ -24,6 +24,8 @@
 //     probabilities the product actually used (v_dot2 with (1, 1)) and normalises O.
 //   * K/V tiles are fetched HBM -> LDS with buffer_load ... lds, double-buffered, so the
 //     next tile's fetch overlaps this tile's math.
+#include <algorithm>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -623,10 +625,15 @@ __global__ __launch_bounds__(256) void fwd16_few_kernel(const Fwd16Params P) {
 // Tiles go through registers into padded LDS rows (K stride D+2, V stride D+8 floats),
 // which keeps both operand reads free of bank conflicts.
 // ----------------------------------------------------------------------------------
-template <int D, int NW, int BC, bool CAUSAL>
+// Split key range (SPLIT): workgroup t covers the tiles [split*ct, split*ct + ct) of its
+// query block and writes the partial (unnormalised o, m, l) to `part` in the layout of the
+// 16-bit kernels' partials (o [s][row][D], then m, l, l [s][row]; rows are (query head,
+// position)), merged by fwd32_merge_kernel.
+template <int D, int NW, int BC, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
                                                         const float* __restrict__ V, float* __restrict__ O,
-                                                        float* __restrict__ LSE, int BH, int G, int Nq, int Nk, float c) {
+                                                        float* __restrict__ LSE, int BH, int G, int Nq, int Nk, float c,
+                                                        int ct, int nsplit, float* __restrict__ part) {
   constexpr int BR = 32 * NW;
   constexpr int NT = NW * 64;
   constexpr int KS = D + 2, VS = D + 8;
@@ -638,7 +645,9 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), half = lane >> 5, c32 = lane & 31;
   const int nqb = (Nq + BR - 1) / BR;
   const int bh = blockIdx.x % BH;
-  int qb = blockIdx.x / BH;
+  const int t = blockIdx.x / BH;
+  int qb = t % nqb;
+  const int split = t / nqb;
   if (CAUSAL) qb = nqb - 1 - qb;
   const int q0 = qb * BR;
   const int qw0 = q0 + 32 * wave;
@@ -665,12 +674,15 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
 
   const int nkt_all = (Nk + BC - 1) / BC;
   const int nkt = CAUSAL ? min(nkt_all, (q0 + BR - 1 + off) / BC + 1) : nkt_all;
+  const int j0 = SPLIT ? split * ct : 0;
+  const int j1 = SPLIT ? min(j0 + ct, nkt) : nkt;
+  if (j0 >= j1) return;  // an empty split: the merge does not read it
   float m = -INFINITY, l = 0.f;
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
 
-  for (int j = 0; j < nkt; ++j) {
+  for (int j = j0; j < j1; ++j) {
     const int k0 = j * BC;
     __syncthreads();  // previous tile fully consumed
     constexpr int V4 = BC * D / 4;  // float4 chunks per tile
@@ -736,6 +748,26 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
   }
 
   const float lt = sum_halves(l);
+  if (SPLIT) {
+    if (qrow >= Nq) return;
+    const size_t nrows = (size_t)BH * Nq;
+    const size_t row = (size_t)split * nrows + (size_t)bh * Nq + qrow;
+    float* prow = part + row * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * half;
+        *(f32x4*)(prow + d) = (f32x4){o[db][4 * g], o[db][4 * g + 1], o[db][4 * g + 2], o[db][4 * g + 3]};
+      }
+    if (half == 0) {
+      float* pm = part + (size_t)nsplit * nrows * D;
+      pm[row] = m;
+      pm[(size_t)nsplit * nrows + row] = lt;
+      pm[(size_t)2 * nsplit * nrows + row] = lt;  // the fp32 P V product uses the unrounded P
+    }
+    return;
+  }
   const float inv = 1.0f / lt;
   if (qrow < Nq) {
     float* orow = O + head + (size_t)qrow * D;
@@ -749,6 +781,45 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
       }
     if (half == 0) LSE[(size_t)bh * Nq + qrow] = (m + log2f(lt)) * kLn2;
   }
+}
+
+// Merge of the fp32 kernel's split partials with the (m, l) rule of the tiled method
+// ("FlashAttention：IO 感知…", 基准/方法设计): with M = max_s m_s and a_s = 2^(m_s - M),
+// O = sum_s a_s o_s / sum_s a_s l_s and lse = M + log2(sum_s a_s l_s) (natural log at the
+// end).  One wave per row (query head, position), D/64 elements per lane.
+template <int D, int NW, int BR, int BC, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) void fwd32_merge_kernel(float* __restrict__ O, float* __restrict__ LSE,
+                                                              const float* __restrict__ part, int BH, int Nq, int Nk,
+                                                              int ct, int nsplit) {
+  const size_t nrows = (size_t)BH * Nq;
+  const size_t g = (size_t)blockIdx.x * NW + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (g >= nrows) return;
+  const int pos = (int)(g % Nq);
+  const int q0 = (pos / BR) * BR;
+  const int nkt_all = (Nk + BC - 1) / BC;
+  const int ktiles = CAUSAL ? min(nkt_all, (q0 + BR - 1 + Nk - Nq) / BC + 1) : nkt_all;
+  const int ns = (ktiles + ct - 1) / ct;  // splits that wrote a partial for this row
+  const float* pm = part + (size_t)nsplit * nrows * D;
+  const float* pl = pm + (size_t)nsplit * nrows;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[s * nrows + g]);
+  constexpr int E = D / 64;
+  float acc[E] = {};
+  float lt = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float ms = pm[s * nrows + g];
+    const float a = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
+    lt += a * pl[s * nrows + g];
+    const float* po = part + (s * nrows + g) * D + E * lane;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] += a * po[e];
+  }
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  float* orow = O + g * D + E * lane;
+#pragma unroll
+  for (int e = 0; e < E; ++e) orow[e] = acc[e] * inv;
+  if (lane == 0) LSE[g] = lt > 0.f ? (M + log2f(lt)) * kLn2 : -INFINITY;
 }
 
 // ----------------------------------------------------------------------------------
@@ -843,9 +914,28 @@ template <int D, bool CAUSAL>
 hipError_t go32(const FwdArgs& a) {
   constexpr int BR = 32 * kNW32;
   const int nqb = (a.Nq + BR - 1) / BR;
-  hipLaunchKernelGGL((fwd32_kernel<D, kNW32, kBC32, CAUSAL>), dim3(a.B * a.Hq * nqb), dim3(kNW32 * 64), 0, a.stream,
-                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.B * a.Hq,
-                     a.Hq / a.Hkv, a.Nq, a.Nk, a.scale * kLog2e);
+  const int BH = a.B * a.Hq;
+  const int nkt = (a.Nk + kBC32 - 1) / kBC32;
+  if (a.nsplit <= 1) {
+    hipLaunchKernelGGL((fwd32_kernel<D, kNW32, kBC32, CAUSAL, false>), dim3(BH * nqb), dim3(kNW32 * 64), 0, a.stream,
+                       (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, BH,
+                       a.Hq / a.Hkv, a.Nq, a.Nk, a.scale * kLog2e, nkt, 1, nullptr);
+    return hipGetLastError();
+  }
+  // split the longest query block's key range (every block's, without causal masking)
+  int max_tiles = nkt;
+  if (CAUSAL) max_tiles = min(nkt, (BR * nqb - 1 + a.Nk - a.Nq) / kBC32 + 1);
+  const int ct = (max_tiles + a.nsplit - 1) / a.nsplit;
+  const int ns = (max_tiles + ct - 1) / ct;
+  hipLaunchKernelGGL((fwd32_kernel<D, kNW32, kBC32, CAUSAL, true>), dim3(BH * nqb * ns), dim3(kNW32 * 64), 0, a.stream,
+                     (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, BH, a.Hq / a.Hkv,
+                     a.Nq, a.Nk, a.scale * kLog2e, ct, a.nsplit, a.part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int NWM = 4;
+  const long nrows = (long)BH * a.Nq;
+  hipLaunchKernelGGL((fwd32_merge_kernel<D, NWM, BR, kBC32, CAUSAL>), dim3((nrows + NWM - 1) / NWM), dim3(NWM * 64), 0,
+                     a.stream, (float*)a.o, a.lse, (const float*)a.part, BH, a.Nq, a.Nk, ct, a.nsplit);
   return hipGetLastError();
 }
 
@@ -876,7 +966,20 @@ int max_block_tiles(int R, int Nq, int Nk) {
 }  // namespace
 
 int fwd_suggest_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d, bool causal, int dtype) {
-  if (dtype == kDtypeF32) return 1;
+  if (dtype == kDtypeF32) {
+    // fp32 kernel: 64-row blocks per query head, 32-key tiles; aim at about 256
+    // workgroups (one per CU), down to one tile per split
+    constexpr int BR = 32 * kNW32;
+    const long wg = (long)B * Hq * ((Nq + BR - 1) / BR);
+    const int nkt = (Nk + kBC32 - 1) / kBC32;
+    const int mt = causal ? std::min(nkt, (int)((BR * ((Nq + BR - 1) / BR) - 1 + Nk - Nq) / kBC32 + 1)) : nkt;
+    long want = (256 + wg - 1) / wg;
+    if (want > mt) want = mt;
+    if (want > 64) want = 64;
+    if (want < 2) return 1;
+    const int ct = (int)((mt + want - 1) / want);
+    return (mt + ct - 1) / ct;
+  }
   if ((long)(Hq / Hkv) * Nq <= kFewRows) {
     // key-parallel kernel: one workgroup per CU (128 KiB of LDS at d = 128), at least
     // kFewMinTiles 64-key tiles per split so that the ring's fill and drain stay small

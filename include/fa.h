@@ -202,15 +202,17 @@ int fa_backward_dkdv_ex(const void* q, const void* k, const void* v, const void*
  * instead of its rows, with three key tiles in flight.
  *   fa_forward_split_count    the split count the library suggests for these arguments
  *                             (1: the unsplit grid already gives each CU two workgroups;
- *                             for groups of at most 32 rows, about one workgroup per CU).
+ *                             for groups of at most 32 rows, and for fp32, about one
+ *                             workgroup per CU).
  *   fa_forward_split_workspace_bytes
  *                             nsplit * B*Hq*Nq * (d + 3) * 4 bytes for nsplit >= 2 (0 for
  *                             nsplit < 2 or > 1024).
  *   fa_forward_split          as fa_forward_ex plus nsplit in [1, 1024] and a 16-byte
  *                             aligned device workspace of at least that size (contents on
  *                             entry ignored; NULL allowed when nsplit == 1, which is exactly
- *                             fa_forward_ex).  16-bit inputs only for nsplit > 1
- *                             (FA_ERR_UNSUPPORTED for fp32).  Two kernels on `stream`.
+ *                             fa_forward_ex).  Any dtype (fp32 splits each 64-row block of a
+ *                             query head into chunks of its 32-key tiles).  Two kernels on
+ *                             `stream`.
  */
 int fa_forward_split_count(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, fa_dtype_t dtype);
 

@@ -194,14 +194,16 @@ def test_split_entry_points_validate_before_launch():
     # every split works, and four reach the target
     assert lib.fa_forward_split_count(1, 8, 8, 4096, 4096, 64, 1, fa.FA_BF16) == 6
     assert lib.fa_forward_split_count(1, 8, 8, 4096, 4096, 64, 0, fa.FA_BF16) == 4
-    assert lib.fa_forward_split_count(1, 1, 1, 256, 256, 64, 0, fa.FA_F32) == 1
+    # the fp32 single head (4 blocks of 64 rows, 8 key tiles of 32): one tile per split
+    assert lib.fa_forward_split_count(1, 1, 1, 256, 256, 64, 0, fa.FA_F32) == 8
+    assert lib.fa_forward_split_count(1, 16, 16, 4096, 4096, 64, 1, fa.FA_F32) == 1
     need = lib.fa_forward_split_workspace_bytes(1, 4, 1, 128, 4)
     args = (P, P, P, P2, P2, 1, 4, 2, 1, 512, 128, ctypes.c_float(0.125), 1)
     assert lib.fa_forward_split(*args, 4, P2, need - 1, fa.FA_BF16, NUL) == FA_ERR_WORKSPACE
     assert lib.fa_forward_split(*args, 4, NUL, need, fa.FA_BF16, NUL) == FA_ERR_WORKSPACE
     assert lib.fa_forward_split(*args, 4, MIS, need, fa.FA_BF16, NUL) == FA_ERR_ALIGN
     assert lib.fa_forward_split(*args, 0, P2, need, fa.FA_BF16, NUL) == FA_ERR_SHAPE
-    assert lib.fa_forward_split(*args, 4, P2, need, fa.FA_F32, NUL) == FA_ERR_UNSUPPORTED
+    assert lib.fa_forward_split(*args, 4, P2, need - 1, fa.FA_F32, NUL) == FA_ERR_WORKSPACE  # fp32 splits too
     bad = (P, P, P, P2, P2, 1, 4, 3, 1, 512, 128, ctypes.c_float(0.125), 1)
     assert lib.fa_forward_split(*bad, 4, P2, need, fa.FA_BF16, NUL) == FA_ERR_SHAPE
 

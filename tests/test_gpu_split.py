@@ -28,6 +28,11 @@ CASES = [
     (1, 8, 1, 4, 1000, 64, "f16", False, 3),         # 32 rows, forced split
     (1, 3, 1, 11, 777, 128, "bf16", True, 2),        # 3 x 11 = 33 rows
     (2, 4, 2, 1, 70, 128, "bf16", True, 1024),       # decode, more splits than key tiles
+    # fp32: 64-row blocks per query head split over their 32-key tiles
+    (1, 1, 1, 256, 256, 64, "f32", False, None),      # the fp32 single-head workload's shape
+    (1, 2, 1, 300, 300, 128, "f32", True, 4),
+    (2, 4, 2, 65, 700, 64, "f32", True, None),
+    (1, 2, 2, 100, 33, 64, "f32", False, 1024),       # more splits than key tiles
 ]
 
 
