@@ -1,7 +1,7 @@
 """Turn the JSON lines that test_gpu_full_size.py appends to $FA_PARITY_RECORD into a
 markdown table (one row per workload and output tensor).
 
-    python tests/parity_table.py gpurun_out/parity.jsonl > table.md
+    python tests/parity_table.py parity.jsonl > table.md
 """
 
 import json
