@@ -25,6 +25,7 @@
 //   * K/V tiles are fetched HBM -> LDS with buffer_load ... lds, double-buffered, so the
 //     next tile's fetch overlaps this tile's math.
 #include <algorithm>
+#include <type_traits>
 
 #include "fa_device.h"
 #include "fa_launch.h"
@@ -48,6 +49,8 @@ namespace fa {
 // MFMAs run another wave's softmax runs on the VALU.
 // ----------------------------------------------------------------------------------
 constexpr float kRescaleSlack = 8.0f;
+// Products the two-phase kernel reads its LDS operands ahead of use.
+constexpr int kPpRing = 6;
 // Largest sum of one lane's probabilities in a tile before the 256-row kernel at d = 64
 // moves its exponent reference: every probability then stays below 2^64, far from fp32
 // overflow.  Skipping the per-tile row max saves about a tenth of the softmax's vector
@@ -405,6 +408,299 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   // the rounded probabilities the P V product used, which makes it an exact weighted
   // average of V rows; the logsumexp uses the fp32 sum.  A row with no visible key (only
   // under a block-sparse mask) gets O = 0 and lse = -inf.
+  const float inv = ltr > 0.f ? 1.0f / ltr : 0.f;
+  uint16_t* orow = P.O + head + (size_t)qrow * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = 32 * db + 8 * g + 4 * half;
+      u32x2 w;
+      w.x = T::pack(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+      w.y = T::pack(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+      *(u32x2*)(orow + d) = w;
+    }
+  if (half == 0) P.LSE[(size_t)bkv * R + qrow] = lt > 0.f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+}
+
+
+// LDS reads that fill the first `ring` slots of the two-phase kernel's operand ring: two
+// per P V operand (the first npv products), one per score operand.
+constexpr int pp_first_reads(int ring, int npv) {
+  int n = 0;
+  for (int i = 0; i < ring; ++i) n += i < npv ? 2 : 1;
+  return n;
+}
+
+// ----------------------------------------------------------------------------------
+// Two-phase schedule at d = 128 (no block mask, no split).  The hardware places waves w
+// and w + 4 of a workgroup on one SIMD, and a wave does not issue past its own MFMA while
+// the matrix core runs it, so only the other wave of the SIMD can fill that time.  Here
+// the two waves of a SIMD are held half a tile apart, so that one runs its products while
+// the other runs its softmax.
+//
+// Every wave runs the same sequence per tile t: the products of tile t (P V of tile
+// t - 1, whose P is in s, then S of tile t into s), then the softmax of tile t.  Waves
+// 0-3 (group A) and 4-7 (group B) pass the workgroup barriers at different points of it:
+//   B:  products(t) | softmax(t)  |
+//   A:  | products(t) | softmax(t)
+// so between two barriers one group multiplies while the other exponentiates.  Barrier
+// k closes phase k - 1; B runs products(t) in phase 2t and A in phase 2t + 1, so both
+// read K_t and V_{t-1} in phases 2t and 2t + 1.
+//
+// Tile fills ride in the score half of each product phase, one 1 KiB load every four
+// products, so that they never stall a wave on the memory pipeline's issue queue: B
+// fetches K_{t+1} in phase 2t (into the buffer K_{t-1} left) and waits for it before
+// the barrier that ends phase 2t + 1; A fetches V_{t+1} in phase 2t + 1, into the buffer
+// of V_{t-1} once its own P V products no longer read it, and waits for it a tile later.
+// Fills past the last tile use an empty buffer range and write zeros.  They are issued
+// as assembly (dma16), which the compiler does not count, so the waits are explicit.
+//
+// Each product's LDS operand is read RING products ahead into a register ring, so the
+// product phase does not wait on LDS with no second wave to cover the wait.  LDS
+// addresses are per-lane offsets held in registers plus constants; bit 15 of each offset
+// selects the buffer and flips after every product phase.  The first product phase
+// multiplies P = 0 by a zeroed V buffer, a wave's tiles past its last visible one get
+// P = 0, and the last phase's scores are discarded, so that every product phase runs the
+// same code.
+//
+// The softmax adds up the 16-bit probabilities with plain fp32 adds of the two halves of
+// each packed pair: a v_dot2 would wait for the matrix core, which the other wave of the
+// SIMD keeps busy in this schedule (measured on gfx950: VALU work with one v_dot2 per pair
+// of scores does not overlap another wave's MFMAs at all; without it, 70-100% of it does).
+// ----------------------------------------------------------------------------------
+template <class T, bool CAUSAL, int RING>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd16_pp_kernel(
+    const Fwd16Params P) {
+  constexpr int D = 128, NW = 8, BR = 32 * NW, BC = 128;
+  constexpr int TB = BC * D * 2;       // bytes of one K or V tile
+  constexpr int KB = BC / 32;          // 32-key accumulator blocks per tile
+  constexpr int DS = D / 16;           // contraction steps over the head dimension
+  constexpr int DB = D / 32;           // 32-wide blocks of the output's head dimension
+  constexpr int NPV = (BC / 16) * DB;  // P V products per tile
+  constexpr int NSC = DS * KB;         // score products per tile
+  constexpr int NPR = NPV + NSC;
+  constexpr int FPW = TB / (4 * 1024); // 1 KiB fills per wave of a group per tile
+  static_assert(RING >= 1 && RING <= 7, "operand ring");
+  static_assert(TB == 32768, "buffer parity is bit 15 of an LDS offset");
+  static_assert(NSC == 4 * FPW, "one fill every four score products");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * TB];  // K0 K1 V0 V1
+  FA_LDS uint8_t* lds = (FA_LDS uint8_t*)(smem);
+
+  const int Nq = P.Nq, Nk = P.Nk, R = P.G * P.Nq;
+  const float c = P.c;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id(), half = lane >> 5, c32 = lane & 31;
+  const int grp = wave >> 2, wg = wave & 3;
+  const int nqb = (R + BR - 1) / BR;
+  const int bkv = blockIdx.x % P.BHkv;
+  int qb = blockIdx.x / P.BHkv;
+  if (CAUSAL) qb = nqb - 1 - qb;  // longest rows first
+  const int q0 = qb * BR;
+  const int qw0 = q0 + 32 * wave;
+  const int qrow = qw0 + c32;
+  const int pos = qrow % Nq;
+  const int off = Nk - Nq;
+  const bool wave_rows = qw0 < R;
+  int wpmin = 0, wpmax = -1;
+  if (wave_rows) pos_range(qw0, min(qw0 + 31, R - 1), Nq, wpmin, wpmax);
+  const int NTL = block_key_tiles<BR, BC, CAUSAL>(q0, R, Nq, Nk);
+  // the wave's rows see the tiles [0, Tw)
+  int Tw = wave_rows ? NTL : 0;
+  if (CAUSAL && wave_rows) Tw = wpmax + off < 0 ? 0 : min(NTL, (wpmax + off) / BC + 1);
+
+  const size_t head = (size_t)bkv * R * D;
+  const size_t kvhead = (size_t)bkv * Nk * D;
+  const auto rq = make_rsrc(P.Q + head, (uint32_t)R * D * 2);
+  // group B fills K tiles into K buffer (t + 1) % 2, group A V tiles into V buffer (t + 1) % 2
+  const uint16_t* fsrc = (grp == 1 ? P.K : P.V) + kvhead;
+  const int fbuf0 = grp == 1 ? 0 : 2;
+
+  // Per-lane LDS offsets, for the buffers of the first product phase (K_0 in buffer 0,
+  // the zeroed V buffer 1).  Score operand of step st (key block kb adds kb * 32 rows):
+  // row c32 of the K tile, chunk 2 st + half.  P V operand of output block db (step ks
+  // adds 16 rows): the two transposing reads of lds_colop, rows r and r + 8.
+  int koff[DS], voff[DB][2];
+#pragma unroll
+  for (int st = 0; st < DS; ++st) koff[st] = tile_off<D>(c32, 2 * st + half);
+  {
+    const int li = lane & 15, g = lane >> 4, h = g >> 1;
+    const int r = 4 * h + (li >> 2);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      const int col = 32 * db + 16 * (g & 1) + 4 * (li & 3);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int rr = r + 8 * e;
+        voff[db][e] = 3 * TB + rr * (D * 2) + ((((col >> 3) ^ swz<D>(rr)) << 4) | ((col & 7) << 1));
+      }
+    }
+  }
+  // A group's fill of one tile: wave wg of the group moves the 1 KiB pieces f * 4 + wg
+  // (f < FPW), i.e. rows 16 f + 4 wg + lane / 16, chunk lane % 16 of each; the swizzle
+  // of those rows depends on the lane and wg only.  The buffer resource is moved to the
+  // tile (base and size), so that rows past the end of the sequence read as zeros.
+  int foff[FPW];
+  {
+    const int frow = 4 * wg + (lane >> 4);
+#pragma unroll
+    for (int f = 0; f < FPW; ++f) foff[f] = (16 * f + frow) * (D * 2) + (((lane & 15) ^ swz<D>(frow)) << 4);
+  }
+  auto tile_rsrc = [&](const uint16_t* base, int tile) __attribute__((always_inline)) -> u32x4 {
+    const long rem = (long)Nk * (D * 2) - (long)tile * TB;  // bytes of the head from the tile on
+    return rsrc_words(base + (size_t)max(tile, 0) * BC * D, rem > 0 ? (uint32_t)rem : 0u);
+  };
+
+  // prologue: K_0 (group B) and V_0 (group A), the zeros of V buffer 1, Q.  A block with
+  // no key tile (only causal masking with Nq > Nk could make one; the library rejects
+  // that shape) would skip the loop.
+  if (NTL > 0) {
+    const u32x4 rs = tile_rsrc(fsrc, 0);
+#pragma unroll
+    for (int f = 0; f < FPW; ++f) dma16(lds + fbuf0 * TB + (f * 4 + wg) * 1024, rs, foff[f]);
+#pragma unroll
+    for (int i = 0; i < TB / (512 * 16); ++i) *(FA_LDS u32x4*)(lds + 3 * TB + (i * 512 + tid) * 16) = (u32x4){};
+  }
+  u32x4 qf[DS];
+#pragma unroll
+  for (int st = 0; st < DS; ++st) qf[st] = buffer_load16(rq, qrow * (D * 2) + ((2 * st + half) << 4));
+
+  float m = -INFINITY, l = 0.f, lr = 0.f;
+  f32x16 o[DB], s[KB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) s[kb] = (f32x16){};
+
+  // Product i < NPV is P V step i / DB of output block i % DB; product NPV + j is score
+  // step j / KB of key block j % KB.
+  auto operand = [&](int i) __attribute__((always_inline)) -> u32x4 {
+    if (i < NPV) {
+      const int ks = i / DB, db = i % DB;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(lds + voff[db][0] + ks * 16 * D * 2));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)(lds + voff[db][1] + ks * 16 * D * 2));
+      const u32x2 a = __builtin_bit_cast(u32x2, lo), b = __builtin_bit_cast(u32x2, hi);
+      return (u32x4){a.x, a.y, b.x, b.y};
+    }
+    const int j = i - NPV;
+    return *(const FA_LDS u32x4*)(lds + koff[j / KB] + (j % KB) * 32 * (D * 2));
+  };
+  // the products of tile t, with this group's fill of tile t + 1
+  auto products = [&](int t) __attribute__((always_inline)) {
+    const u32x4 rs = tile_rsrc(fsrc, t + 1);
+    FA_LDS uint8_t* fdst = lds + (fbuf0 + ((t + 1) & 1)) * TB + wg * 1024;
+    u32x4 ring[RING];
+#pragma unroll
+    for (int i = 0; i < RING; ++i) ring[i] = operand(i);
+#pragma unroll
+    for (int i = 0; i < NPR; ++i) {
+      const u32x4 a = ring[i % RING];
+      if (i + RING < NPR) ring[i % RING] = operand(i + RING);
+      if (i < NPV) {
+        const int ks = i / DB, db = i % DB, kb = ks >> 1, mm = ks & 1;
+        const u32x4 b = (u32x4){__float_as_uint(s[kb][4 * mm]), __float_as_uint(s[kb][4 * mm + 1]),
+                                __float_as_uint(s[kb][4 * mm + 2]), __float_as_uint(s[kb][4 * mm + 3])};
+        o[db] = T::mfma(a, b, o[db]);
+      } else {
+        const int j = i - NPV, st = j / KB, kb = j % KB;
+        s[kb] = T::mfma(a, qf[st], st == 0 ? (f32x16){} : s[kb]);
+        // after the last P V product: its V buffer may be refilled
+        if (j % 4 == 0) dma16(fdst + (j / 4) * 4 * 1024, rs, foff[j / 4]);
+      }
+    }
+    // issue order: the ring's first reads, then each product followed by the reads of
+    // the product RING places later
+    constexpr int FIRST = pp_first_reads(RING, NPV);
+    __builtin_amdgcn_sched_group_barrier(0x100, FIRST, 0);
+#pragma unroll
+    for (int i = 0; i < NPR; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i + RING < NPR) {
+        if (i + RING < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    // the next product phase reads the other K and V buffers
+#pragma unroll
+    for (int st = 0; st < DS; ++st) koff[st] ^= TB;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      voff[db][0] ^= TB;
+      voff[db][1] ^= TB;
+    }
+  };
+
+  // softmax of tile t: masks, row max, lazy rescale, exponentials, sums, 16-bit P.  A
+  // tile past the wave's last visible one gets P = 0.
+  auto softmax_of = [&](int t) __attribute__((always_inline)) {
+    if (t >= Tw) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 8; ++t2) s[kb][t2] = 0.f;
+      return;
+    }
+    const int k0 = t * BC;
+    if ((k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > wpmin + off)) {
+      // keys past the end and (causal) after the row's position: the key's offset in the
+      // tile, a constant per register, against the lane's last visible offset
+      const int lim = (CAUSAL ? min(pos + off, Nk - 1) : Nk - 1) - k0 - 4 * half;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] = 32 * kb + acc_row(i, 0) > lim ? -INFINITY : s[kb][i];
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) mx = max_nan(max_nan(mx, s[kb][i]), s[kb][i + 1]);
+    mx = max_halves(mx) * c;
+    if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m - m_new);  // o, l are 0 while m = -inf
+      l *= alpha;
+      lr *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      m = m_new;
+    }
+    const float mu = (m == -INFINITY) ? 0.f : m;  // every score of such a row is -inf: p = 0
+    float rs = 0.f, rsr = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int t2 = 0; t2 < 8; ++t2) {
+        const float p0 = fast_exp2(fmaf(s[kb][2 * t2], c, -mu));
+        const float p1 = fast_exp2(fmaf(s[kb][2 * t2 + 1], c, -mu));
+        rs += p0 + p1;
+        const uint32_t pk = T::pack(p0, p1);
+        rsr += T::lo_f32(pk) + T::hi_f32(pk);
+        s[kb][t2] = __uint_as_float(pk);
+      }
+    l += rs;
+    lr += rsr;
+  };
+
+  // Q, K_0 (and V_0) have landed; the wait also settles the compiler's count of the Q
+  // loads, so that no wait for them is left inside the loop (where it would count the
+  // fills in flight too)
+  wait_vmem();
+  __syncthreads();  // barrier 0: K_0, V_0 and the zeros are in LDS
+  for (int t = 0; t <= NTL && NTL > 0; ++t) {
+    if (grp == 0) __syncthreads();  // A: barrier 2t + 1
+    products(t);
+    if (grp == 0) wait_vmem_upto<FPW>();  // A: V_t (fetched a tile ago) has landed
+    __syncthreads();                      // A: barrier 2t + 2, B: barrier 2t + 1
+    softmax_of(t);
+    if (grp == 1) {
+      wait_vmem();      // B: K_{t+1} has landed
+      __syncthreads();  // B: barrier 2t + 2
+    }
+  }
+
+  const float lt = sum_halves(l);
+  const float ltr = sum_halves(lr);
+  if (qrow >= R) return;
   const float inv = ltr > 0.f ? 1.0f / ltr : 0.f;
   uint16_t* orow = P.O + head + (size_t)qrow * D;
 #pragma unroll
@@ -880,6 +1176,10 @@ hipError_t go16(const FwdArgs& a) {
   if (!SPARSE && R <= kFewRows) return go_few<T, D, CAUSAL>(a, p);
   if (a.nsplit <= 1) {
     p.ct = (a.Nk + S::BC - 1) / S::BC;
+    if constexpr (D == 128 && !SPARSE) {
+      hipLaunchKernelGGL((fwd16_pp_kernel<T, CAUSAL, kPpRing>), dim3(BHkv * nqb), dim3(512), 0, a.stream, p);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL((fwd16_kernel<T, D, S::NW, S::BC, S::WPE, CAUSAL, false, SPARSE>), dim3(BHkv * nqb),
                        dim3(S::NW * 64), 0, a.stream, p);
     return hipGetLastError();
