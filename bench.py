@@ -72,7 +72,7 @@ def stored_traffic(kernel: str, workload: str):
         return None
 
 
-KERNEL_KEYS = (("fwd16_kernel", "fwd"), ("fwd32_kernel", "fwd"), ("bwd_dq_kernel", "bwd_dq"),
+KERNEL_KEYS = (("fwd16_kernel", "fwd"), ("fwd16_pp_kernel", "fwd"), ("fwd32_kernel", "fwd"), ("bwd_dq_kernel", "bwd_dq"),
                ("bwd_dkdv_kernel", "bwd_dkdv"))
 
 
