@@ -131,13 +131,17 @@ __device__ __forceinline__ bool rows_need_tile(const Fwd16Params& P, int bkv, in
 // Merge of the split partials of one packed row with the (m, l) rule of the tiled
 // method ("FlashAttention：IO 感知…", 基准/方法设计): with M = max_s m_s and
 // a_s = 2^(m_s - M), O = sum_s a_s o_s / sum_s a_s lr_s and lse = M + log2(sum_s a_s l_s)
-// (base 2, converted to natural log).  One wave per row, D/64 elements per lane.
-template <class T, int D, int NW, int BR, int BC, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) void fwd_merge_kernel(const Fwd16Params P) {
+// (base 2, converted to natural log).  D / E lanes per row, E columns each (E = 4 for
+// the 256-row kernel's many rows, E = 2 for the few-row kernel's handful).
+template <class T, int D, int E, int BR, int BC, bool CAUSAL>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(const Fwd16Params P) {
+  static_assert(E == 2 || E == 4, "columns per lane");
+  constexpr int LPR = D / E;      // lanes per row
+  constexpr int RPB = 256 / LPR;  // rows per workgroup
   const int R = P.G * P.Nq;
   const size_t nrows = (size_t)P.BHkv * R;
-  const size_t g = (size_t)blockIdx.x * NW + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
+  const size_t g = (size_t)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int c0 = (threadIdx.x % LPR) * E;
   if (g >= nrows) return;
   const int r = (int)(g % R);
   const int ktiles = block_key_tiles<BR, BC, CAUSAL>((r / BR) * BR, R, P.Nq, P.Nk);
@@ -147,27 +151,36 @@ __global__ __launch_bounds__(NW * 64) void fwd_merge_kernel(const Fwd16Params P)
   const float* plr = pl + (size_t)P.nsplit * nrows;
   float M = -INFINITY;
   for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[s * nrows + g]);  // -inf only for a row with no visible key
-  constexpr int E = D / 64;
   float acc[E] = {};
   float lt = 0.f, lr = 0.f;
+#pragma unroll(E == 4 ? 4 : 1)
   for (int s = 0; s < ns; ++s) {
     const float ms = pm[s * nrows + g];
     const float a = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
     lt += a * pl[s * nrows + g];
     lr += a * plr[s * nrows + g];
-    const float* po = P.part + (s * nrows + g) * D + E * lane;
+    const float* po = P.part + (s * nrows + g) * D + c0;
+    if constexpr (E == 4) {
+      const f32x4 v = *(const f32x4*)po;
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] += a * po[e];
+      for (int e = 0; e < 4; ++e) acc[e] += a * v[e];
+    } else {
+      const f32x2 v = *(const f32x2*)po;
+      acc[0] += a * v[0];
+      acc[1] += a * v[1];
+    }
   }
   const float inv = lr > 0.f ? 1.0f / lr : 0.f;
-  uint16_t* orow = P.O + g * D + E * lane;
-  if constexpr (E == 2) {
-    *(uint32_t*)orow = T::pack(acc[0] * inv, acc[1] * inv);
+  uint16_t* orow = P.O + g * D + c0;
+  if constexpr (E == 4) {
+    u32x2 w;
+    w.x = T::pack(acc[0] * inv, acc[1] * inv);
+    w.y = T::pack(acc[2] * inv, acc[3] * inv);
+    *(u32x2*)orow = w;
   } else {
-    const uint32_t w = T::pack(acc[0] * inv, 0.f);
-    *orow = (uint16_t)(w & 0xffffu);
+    *(uint32_t*)orow = T::pack(acc[0] * inv, acc[1] * inv);
   }
-  if (lane == 0) P.LSE[g] = lt > 0.f ? (M + log2f(lt)) * kLn2 : -INFINITY;
+  if (c0 == 0) P.LSE[g] = lt > 0.f ? (M + log2f(lt)) * kLn2 : -INFINITY;
 }
 
 template <class T, int D, int NW, int BC, int WPE, bool CAUSAL, bool SPLIT, bool SPARSE>
@@ -1155,10 +1168,11 @@ hipError_t go_few(const FwdArgs& a, Fwd16Params p) {
   hipLaunchKernelGGL((fwd16_few_kernel<T, D, CAUSAL, true>), dim3(p.BHkv * ns), dim3(256), 0, a.stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int NWM = 4;
+  // few rows: two columns per lane, more lanes per row
   const long nrows = (long)p.BHkv * R;
-  hipLaunchKernelGGL((fwd_merge_kernel<T, D, NWM, kFewRows, BC, CAUSAL>), dim3((nrows + NWM - 1) / NWM),
-                     dim3(NWM * 64), 0, a.stream, p);
+  constexpr int RPB = 256 / (D / 2);
+  hipLaunchKernelGGL((fwd_merge_kernel<T, D, 2, kFewRows, BC, CAUSAL>), dim3((nrows + RPB - 1) / RPB), dim3(256), 0,
+                     a.stream, p);
   return hipGetLastError();
 }
 
@@ -1198,10 +1212,10 @@ hipError_t go16(const FwdArgs& a) {
                      dim3(S::NW * 64), 0, a.stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int NWM = 4;
   const long nrows = (long)BHkv * R;
-  hipLaunchKernelGGL((fwd_merge_kernel<T, D, NWM, BR, S::BC, CAUSAL>), dim3((nrows + NWM - 1) / NWM), dim3(NWM * 64),
-                     0, a.stream, p);
+  constexpr int RPB = 256 / (D / 4);
+  hipLaunchKernelGGL((fwd_merge_kernel<T, D, 4, BR, S::BC, CAUSAL>), dim3((nrows + RPB - 1) / RPB), dim3(256), 0,
+                     a.stream, p);
   return hipGetLastError();
 }
 
