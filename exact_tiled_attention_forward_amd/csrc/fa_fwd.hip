@@ -461,13 +461,14 @@ constexpr int pp_first_reads(int ring, int npv) {
 // k closes phase k - 1; B runs products(t) in phase 2t and A in phase 2t + 1, so both
 // read K_t and V_{t-1} in phases 2t and 2t + 1.
 //
-// Tile fills ride in the score half of each product phase, one 1 KiB load every four
-// products, so that they never stall a wave on the memory pipeline's issue queue: B
-// fetches K_{t+1} in phase 2t (into the buffer K_{t-1} left) and waits for it before
-// the barrier that ends phase 2t + 1; A fetches V_{t+1} in phase 2t + 1, into the buffer
-// of V_{t-1} once its own P V products no longer read it, and waits for it a tile later.
-// Fills past the last tile use an empty buffer range and write zeros.  They are issued
-// as assembly (dma16), which the compiler does not count, so the waits are explicit.
+// Tile fills are spread out, one 1 KiB load at a time, so that they never stall a wave on
+// the memory pipeline's issue queue.  B fetches K_{t+1} in the score half of its products
+// (phase 2t, into the buffer K_{t-1} left) and waits for it before the barrier that ends
+// phase 2t + 1.  A fetches V_{t+1} during its softmax of tile t (phase 2t + 2, into the
+// buffer V_{t-1} left: the products of tile t read it in phases 2t and 2t + 1, so no
+// earlier phase is free of readers) and waits for it a tile later.  Rows past the end of
+// the sequence read as zeros.  The fills are issued as assembly (dma16), which the
+// compiler does not count, so the waits are explicit.
 //
 // Each product's LDS operand is read RING products ahead into a register ring, so the
 // product phase does not wait on LDS with no second wave to cover the wait.  LDS
@@ -570,8 +571,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const u32x4 rs = tile_rsrc(fsrc, 0);
 #pragma unroll
     for (int f = 0; f < FPW; ++f) dma16(lds + fbuf0 * TB + (f * 4 + wg) * 1024, rs, foff[f]);
-#pragma unroll
-    for (int i = 0; i < TB / (512 * 16); ++i) *(FA_LDS u32x4*)(lds + 3 * TB + (i * 512 + tid) * 16) = (u32x4){};
   }
   u32x4 qf[DS];
 #pragma unroll
@@ -597,40 +596,49 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int j = i - NPV;
     return *(const FA_LDS u32x4*)(lds + koff[j / KB] + (j % KB) * 32 * (D * 2));
   };
-  // the products of tile t, with this group's fill of tile t + 1
+  // The products of tile t.  Each half runs only where it contributes: P V of tile t - 1
+  // if the wave's rows see that tile, S of tile t if they see this one.  Each half streams
+  // its own operands through the ring.  Group B fetches K_{t+1} in the S half, one 1 KiB
+  // load every four products (in a row when the S half does not run).
   auto products = [&](int t) __attribute__((always_inline)) {
     const u32x4 rs = tile_rsrc(fsrc, t + 1);
     FA_LDS uint8_t* fdst = lds + (fbuf0 + ((t + 1) & 1)) * TB + wg * 1024;
-    u32x4 ring[RING];
+    auto half_of = [&](auto first, auto count) __attribute__((always_inline)) {
+      constexpr int I0 = decltype(first)::value, N = decltype(count)::value;
+      u32x4 ring[RING];
 #pragma unroll
-    for (int i = 0; i < RING; ++i) ring[i] = operand(i);
+      for (int i = 0; i < RING; ++i) ring[i] = operand(I0 + i);
 #pragma unroll
-    for (int i = 0; i < NPR; ++i) {
-      const u32x4 a = ring[i % RING];
-      if (i + RING < NPR) ring[i % RING] = operand(i + RING);
-      if (i < NPV) {
-        const int ks = i / DB, db = i % DB, kb = ks >> 1, mm = ks & 1;
-        const u32x4 b = (u32x4){__float_as_uint(s[kb][4 * mm]), __float_as_uint(s[kb][4 * mm + 1]),
-                                __float_as_uint(s[kb][4 * mm + 2]), __float_as_uint(s[kb][4 * mm + 3])};
-        o[db] = T::mfma(a, b, o[db]);
-      } else {
-        const int j = i - NPV, st = j / KB, kb = j % KB;
-        s[kb] = T::mfma(a, qf[st], st == 0 ? (f32x16){} : s[kb]);
-        // after the last P V product: its V buffer may be refilled
-        if (j % 4 == 0) dma16(fdst + (j / 4) * 4 * 1024, rs, foff[j / 4]);
+      for (int i = I0; i < I0 + N; ++i) {
+        const u32x4 a = ring[(i - I0) % RING];
+        if (i + RING < I0 + N) ring[(i - I0) % RING] = operand(i + RING);
+        if (i < NPV) {
+          const int ks = i / DB, db = i % DB, kb = ks >> 1, mm = ks & 1;
+          const u32x4 b = (u32x4){__float_as_uint(s[kb][4 * mm]), __float_as_uint(s[kb][4 * mm + 1]),
+                                  __float_as_uint(s[kb][4 * mm + 2]), __float_as_uint(s[kb][4 * mm + 3])};
+          o[db] = T::mfma(a, b, o[db]);
+        } else {
+          const int j = i - NPV, st = j / KB, kb = j % KB;
+          s[kb] = T::mfma(a, qf[st], st == 0 ? (f32x16){} : s[kb]);
+          if (j % 4 == 0 && grp == 1) dma16(fdst + (j / 4) * 4 * 1024, rs, foff[j / 4]);
+        }
       }
-    }
-    // issue order: the ring's first reads, then each product followed by the reads of
-    // the product RING places later
-    constexpr int FIRST = pp_first_reads(RING, NPV);
-    __builtin_amdgcn_sched_group_barrier(0x100, FIRST, 0);
+      // issue order: the ring's first reads, then each product followed by the reads of
+      // the product RING places later
+      constexpr int FIRST = RING * (I0 < NPV ? 2 : 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, FIRST, 0);
 #pragma unroll
-    for (int i = 0; i < NPR; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i + RING < NPR) {
-        if (i + RING < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = I0; i < I0 + N; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i + RING < I0 + N) __builtin_amdgcn_sched_group_barrier(0x100, I0 < NPV ? 2 : 1, 0);
       }
+    };
+    if (t >= 1 && t - 1 < Tw) half_of(std::integral_constant<int, 0>{}, std::integral_constant<int, NPV>{});
+    if (t < Tw) {
+      half_of(std::integral_constant<int, NPV>{}, std::integral_constant<int, NSC>{});
+    } else if (grp == 1 && t + 1 < NTL) {
+#pragma unroll
+      for (int f = 0; f < FPW; ++f) dma16(fdst + f * 4 * 1024, rs, foff[f]);
     }
     // the next product phase reads the other K and V buffers
 #pragma unroll
@@ -642,14 +650,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   };
 
-  // softmax of tile t: masks, row max, lazy rescale, exponentials, sums, 16-bit P.  A
-  // tile past the wave's last visible one gets P = 0.
+  // Group A fetches V_{t+1} during its softmax of tile t (phase 2t + 2, when no wave reads
+  // the buffer V_{t-1} left), one 1 KiB load every four pairs of exponentials.
+  auto vfill = [&](int t, int f) __attribute__((always_inline)) {
+    if (grp == 0 && t + 1 < NTL)
+      dma16(lds + (fbuf0 + ((t + 1) & 1)) * TB + (f * 4 + wg) * 1024, tile_rsrc(fsrc, t + 1), foff[f]);
+  };
+  // softmax of tile t: masks, row max, lazy rescale, exponentials, sums, 16-bit P (none
+  // past the wave's last visible tile)
   auto softmax_of = [&](int t) __attribute__((always_inline)) {
     if (t >= Tw) {
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int t2 = 0; t2 < 8; ++t2) s[kb][t2] = 0.f;
+      for (int f = 0; f < FPW; ++f) vfill(t, f);
       return;
     }
     const int k0 = t * BC;
@@ -689,6 +701,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const uint32_t pk = T::pack(p0, p1);
         rsr += T::lo_f32(pk) + T::hi_f32(pk);
         s[kb][t2] = __uint_as_float(pk);
+        if (t2 % 4 == 0) vfill(t, 2 * kb + t2 / 4);
       }
     l += rs;
     lr += rsr;
@@ -702,7 +715,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int t = 0; t <= NTL && NTL > 0; ++t) {
     if (grp == 0) __syncthreads();  // A: barrier 2t + 1
     products(t);
-    if (grp == 0) wait_vmem_upto<FPW>();  // A: V_t (fetched a tile ago) has landed
+    if (grp == 0) wait_vmem();  // A: V_t (fetched during its previous softmax) has landed
     __syncthreads();                      // A: barrier 2t + 2, B: barrier 2t + 1
     softmax_of(t);
     if (grp == 1) {
@@ -711,6 +724,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
   }
 
+  wait_vmem();  // no fill may outlive the workgroup's LDS
   const float lt = sum_halves(l);
   const float ltr = sum_halves(lr);
   if (qrow >= R) return;
