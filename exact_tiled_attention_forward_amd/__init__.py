@@ -24,9 +24,11 @@ import torch  # the HIP runtime torch loads is the one libfa.so binds to (same s
 
 __all__ = ["MASK_BLOCK", "fa_forward", "fa_forward_fp8", "fa_quantize_fp8", "fa_forward_split_count", "fa_backward", "fa_backward_dq", "fa_backward_dkdv", "fa_backward_noalloc",
            "fa_backward_workspace_bytes",
-           "library", "FAError", "FA_F32", "FA_F16", "FA_BF16", "LIB_PATH"]
+           "library", "load_library", "FAError", "FA_F32", "FA_F16", "FA_BF16", "LIB_PATH", "RACECHECK_LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+# the race-check build (same results on a perturbed schedule; see csrc/fa_device.h)
+RACECHECK_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_racecheck.so")
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
@@ -47,9 +49,16 @@ def library() -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m exact_tiled_attention_forward_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
+    _lib = load_library(LIB_PATH)
+    return _lib
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """A build of the library at `path` with its C signatures declared (the release build
+    is `library()`; the race-check build is RACECHECK_LIB_PATH)."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m exact_tiled_attention_forward_amd.build`")
+    lib = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_forward.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
     lib.fa_forward.restype = i
@@ -92,7 +101,6 @@ def library() -> ctypes.CDLL:
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
     lib.fa_version.restype = i
-    _lib = lib
     return lib
 
 

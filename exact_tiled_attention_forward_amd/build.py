@@ -23,6 +23,9 @@ LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 
 SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_fp8.hip", "fa_api.cpp"]
+# The race-check build: the same sources with -DFA_RACE_CHECK=1 (perturbed schedule,
+# identical results; see csrc/fa_device.h).  Only the race-check tests load it.
+RACECHECK_LIB = os.path.join(PKG, "libfa_racecheck.so")
 
 
 def hipcc() -> str:
@@ -46,9 +49,13 @@ def common_flags():
     ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *common_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, variant = job
+    outdir = os.path.join(BUILD, variant) if variant else BUILD
+    os.makedirs(outdir, exist_ok=True)
+    obj = os.path.join(outdir, os.path.splitext(src)[0] + ".o")
+    extra = ["-DFA_RACE_CHECK=1"] if variant == "racecheck" else []
+    cmd = [hipcc(), *common_flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -59,18 +66,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {lib}")
+
+
+def build(verbose: bool = False) -> str:
+    """Build libfa.so and the race-check build libfa_racecheck.so; returns the former."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = [(src, "") for src in SOURCES] + [(src, "racecheck") for src in SOURCES]
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        objs = list(ex.map(_compile, jobs))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], RACECHECK_LIB, verbose)
     return LIB
 
 

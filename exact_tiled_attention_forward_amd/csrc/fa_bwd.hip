@@ -114,7 +114,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   // branch, so that no score pays for the other pass or for the mask test
   auto run_pass = [&](auto pass_tag) {
     constexpr int pass = decltype(pass_tag)::value;
-    __syncthreads();  // the previous pass is done with both LDS buffers
+    fa_sync();  // the previous pass is done with both LDS buffers
     int j = next_tile(0);
     if (j < nkt) {
       tile_load_async<D, BC, NT>(lds, rk, j * BC, tid);
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     }
     for (int cur = 0; j < nkt; cur ^= 1) {
       wait_vmem();
-      __syncthreads();
+      fa_sync();
       const int jn = next_tile(j + 1);
       if (jn < nkt) {
         tile_load_async<D, BC, NT>(lds + (cur ^ 1) * TB, rk, jn * BC, tid);
@@ -271,6 +271,7 @@ __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(WPE
                                                0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (FA_LDS void*)(stats + buf * 128 + 64), 4,
                                                (qt * BQ + lane) * 4, 0, 0, 0);
+      race_check_fill_wait();
     }
   };
 
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(WPE
 
   for (int cur = 0; t < ntiles; cur ^= 1) {
     wait_vmem();
-    __syncthreads();
+    fa_sync();
     const int tn = next_tile(t + 1);
     if (tn < ntiles) load_tile(tn, cur ^ 1);
     const int q0 = (qt0 + t % nt) * BQ;
@@ -400,7 +401,7 @@ __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(WPE
         else probabilities(std::false_type{});
       }
     }
-    __syncthreads();
+    fa_sync();
     if (!active) continue;
 
     // phase 2: A: dV^T += dO^T (P hi + P lo);  B: dS = P (dP - D), dK^T += Q^T (dS hi + dS lo)

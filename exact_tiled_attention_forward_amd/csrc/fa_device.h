@@ -39,6 +39,21 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 #define FA_LDS __attribute__((address_space(3)))
 
+// Race-check build (-DFA_RACE_CHECK=1, libfa_racecheck.so).  Its kernels compute exactly
+// what the release build computes, on a perturbed schedule: after every workgroup barrier
+// each wave sleeps for a time that grows with its index modulo 4, so that within each set
+// of four waves (the two groups of the two-phase forward) the first wave runs ahead of the
+// last by longer than a tile fill takes to land, and every tile fill waits for its own
+// completion as soon as it is issued, so that it lands as early as it can.  A fill that
+// overwrites a buffer some wave may still read, or a read that does not wait for its
+// fill, then changes the result: the race-check tests compare both builds bit for bit.
+// Checked against an earlier forward whose V fill was issued while waves of its own group
+// could still be reading the buffer: the release and race-check builds of that kernel
+// differed on every test case.
+#ifndef FA_RACE_CHECK
+#define FA_RACE_CHECK 0
+#endif
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;  // raw buffer, 32-bit dwords (gfx9 family)
@@ -152,6 +167,24 @@ __device__ __forceinline__ u32x4 lds_colop(const FA_LDS uint8_t* tile, int rbase
 // instead of branched over.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
 
+// Race-check build only: wait for this wave's outstanding loads (a fill just issued).
+__device__ __forceinline__ void race_check_fill_wait() {
+#if FA_RACE_CHECK
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+#endif
+}
+
+// Workgroup barrier.  In the race-check build each wave then sleeps about 4000 cycles
+// per unit of its index modulo 4 (waves 0-3 and 4-7 each fan out over about 12000 cycles,
+// longer than a tile fill takes to land).
+__device__ __forceinline__ void fa_sync() {
+  __syncthreads();
+#if FA_RACE_CHECK
+  const int w = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) & 3;
+  for (int i = 0; i < 8 * w; ++i) __builtin_amdgcn_s_sleep(8);
+#endif
+}
+
 // Fill `rows` x D tile (16-bit) from global rows [row0, row0 + rows) of a head whose
 // buffer resource covers exactly that head.  NT threads cooperate; each wave instruction
 // moves 1 KiB.  Out-of-range rows read as zeros.
@@ -172,6 +205,7 @@ __device__ __forceinline__ void tile_load_async(FA_LDS uint8_t* tile, __amdgpu_b
     const int c = slot ^ swz<D>(r);
     const int voff = (row0 + r) * (D * 2) + (c << 4);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)(tile + base * 16), 16, voff, 0, 0, 0);
+    race_check_fill_wait();
   };
   if constexpr (NI % WAVES == 0) {
 #pragma unroll
@@ -195,10 +229,17 @@ __device__ __forceinline__ void tile_load_async(FA_LDS uint8_t* tile, __amdgpu_b
 __device__ __forceinline__ void dma16(const FA_LDS void* lds_dst, const u32x4& rs, int voff) {
   // wave-uniform LDS byte address, moved to an SGPR for the s_mov
   const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_dst);
+#if FA_RACE_CHECK
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds\n\ts_waitcnt vmcnt(0)"
+               :
+               : "s"(m0), "v"(voff), "s"(rs)
+               : "memory", "m0");
+#else
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(m0), "v"(voff), "s"(rs)
                : "memory", "m0");
+#endif
 }
 #pragma clang diagnostic pop
 

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const In* __restrict__ 
   for (int i = threadIdx.x; i < count; i += 256) amax = fmaxf(amax, fabsf(load_as_f32(x, base + i)));
   for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
-  __syncthreads();
+  fa_sync();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = amax > 0.f ? amax / kE4m3Max : 1.0f;
   if (threadIdx.x == 0) scales[(size_t)bh * nb + blk] = s;
@@ -167,6 +167,7 @@ __device__ __forceinline__ void tile8_load_async(FA_LDS uint8_t* tile, __amdgpu_
     const int ch = (slot ^ (r % CPR)) & (CPR - 1);  // global chunk stored at this slot
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (FA_LDS void*)(tile + base * 16), 16, (row0 + r) * D + (ch << 4), 0,
                                              0, 0);
+    race_check_fill_wait();
   };
   if constexpr (NI % WAVES == 0) {
 #pragma unroll
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   for (int j = 0; j < nkt; ++j) {
     wait_vmem();
-    __syncthreads();
+    fa_sync();
     const int cur = j & 1;
     if (j + 1 < nkt) {
       tile8_load_async<D, BC, NT>(lds + (cur ^ 1) * TB, rk, (j + 1) * BC, tid);

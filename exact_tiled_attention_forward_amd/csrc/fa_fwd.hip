@@ -261,7 +261,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 
   for (int cur = 0; j < j1; cur ^= 1) {
     wait_vmem();
-    __syncthreads();
+    fa_sync();
     const int jn = next_tile(j + 1);
     if (jn < j1) {
       tile_load_async<D, BC, NT>(lds + (cur ^ 1) * TB, rk, jn * BC, tid);
@@ -711,16 +711,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // loads, so that no wait for them is left inside the loop (where it would count the
   // fills in flight too)
   wait_vmem();
-  __syncthreads();  // barrier 0: K_0, V_0 and the zeros are in LDS
+  fa_sync();  // barrier 0: K_0, V_0 and the zeros are in LDS
   for (int t = 0; t <= NTL && NTL > 0; ++t) {
-    if (grp == 0) __syncthreads();  // A: barrier 2t + 1
+    if (grp == 0) fa_sync();  // A: barrier 2t + 1
     products(t);
     if (grp == 0) wait_vmem();  // A: V_t (fetched during its previous softmax) has landed
-    __syncthreads();                      // A: barrier 2t + 2, B: barrier 2t + 1
+    fa_sync();                      // A: barrier 2t + 2, B: barrier 2t + 1
     softmax_of(t);
     if (grp == 1) {
       wait_vmem();      // B: K_{t+1} has landed
-      __syncthreads();  // B: barrier 2t + 2
+      fa_sync();  // B: barrier 2t + 2
     }
   }
 
@@ -805,7 +805,7 @@ __global__ __launch_bounds__(256) void fwd16_few_kernel(const Fwd16Params P) {
   if (n >= ST - 1) wait_vmem_upto<(ST - 1) * LPT>();  // the query rows have landed
   else if (n == 2) wait_vmem_upto<2 * LPT>();
   else wait_vmem_upto<LPT>();
-  __syncthreads();
+  fa_sync();
   u32x4 qf[DS];
 #pragma unroll
   for (int st = 0; st < DS; ++st) qf[st] = lds_row16<D>(qt, qrow, 2 * st + half);
@@ -822,7 +822,7 @@ __global__ __launch_bounds__(256) void fwd16_few_kernel(const Fwd16Params P) {
     if (t + 2 < n) wait_vmem_upto<2 * LPT>();
     else if (t + 1 < n) wait_vmem_upto<LPT>();
     else wait_vmem_upto<0>();
-    __syncthreads();  // every wave's part of tile t is in LDS; stage (t - 1) % ST is free
+    fa_sync();  // every wave's part of tile t is in LDS; stage (t - 1) % ST is free
     if (t + ST - 1 < n) load(t + ST - 1);
     if ((t & 1) != parity) continue;
     const int k0 = (j0 + t) * BC + 32 * kb;  // this wave's 32 keys
@@ -876,7 +876,7 @@ __global__ __launch_bounds__(256) void fwd16_few_kernel(const Fwd16Params P) {
 
   // merge the four waves' states: o [w][row][D], then m, l, lr [w][row]
   const float lt = sum_halves(l), ltr = sum_halves(lr);
-  __syncthreads();  // every wave is done with the ring
+  fa_sync();  // every wave is done with the ring
   float* xo = (float*)smem;
   float* xm = xo + 4 * 32 * D;
 #pragma unroll
@@ -891,7 +891,7 @@ __global__ __launch_bounds__(256) void fwd16_few_kernel(const Fwd16Params P) {
     xm[128 + wave * 32 + c32] = lt;
     xm[256 + wave * 32 + c32] = ltr;
   }
-  __syncthreads();
+  fa_sync();
   // thread -> (row, 16 consecutive columns)
   constexpr int CPT = D * 32 / NT;
   const int r = tid / (D / CPT), d0 = (tid % (D / CPT)) * CPT;
@@ -1007,7 +1007,7 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
 
   for (int j = j0; j < j1; ++j) {
     const int k0 = j * BC;
-    __syncthreads();  // previous tile fully consumed
+    fa_sync();  // previous tile fully consumed
     constexpr int V4 = BC * D / 4;  // float4 chunks per tile
     for (int p = tid; p < V4; p += NT) {
       const int r = p / (D / 4), cc = (p % (D / 4)) * 4;
@@ -1018,7 +1018,7 @@ __global__ __launch_bounds__(NW * 64) void fwd32_kernel(const float* __restrict_
       *(f32x2*)(kd + 2) = (f32x2){__uint_as_float(kw.z), __uint_as_float(kw.w)};
       *(u32x4*)(vs_ + r * VS + cc) = vw;
     }
-    __syncthreads();
+    fa_sync();
     if (CAUSAL && k0 > qw0 + 31 + off) continue;
 
     f32x16 s[KB];
