@@ -79,6 +79,11 @@ struct bf16_t {
   }
   static __device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
   static __device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+  static constexpr uint32_t kOnePair = 0x3f803f80u;  // (1, 1)
+  static __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
 };
 
 struct f16_t {
@@ -98,6 +103,11 @@ struct f16_t {
   }
   static __device__ __forceinline__ float lo_f32(uint32_t w) { return to_f32((uint16_t)(w & 0xffffu)); }
   static __device__ __forceinline__ float hi_f32(uint32_t w) { return to_f32((uint16_t)(w >> 16)); }
+  static constexpr uint32_t kOnePair = 0x3c003c00u;  // (1, 1)
+  static __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
 };
 
 // Two fp32 values as a 16-bit pair hi plus the 16-bit pair of what hi missed, so that

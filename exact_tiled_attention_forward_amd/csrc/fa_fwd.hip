@@ -478,10 +478,12 @@ constexpr int pp_first_reads(int ring, int npv) {
 // P = 0, and the last phase's scores are discarded, so that every product phase runs the
 // same code.
 //
-// The softmax adds up the 16-bit probabilities with plain fp32 adds of the two halves of
-// each packed pair: a v_dot2 would wait for the matrix core, which the other wave of the
-// SIMD keeps busy in this schedule (measured on gfx950: VALU work with one v_dot2 per pair
-// of scores does not overlap another wave's MFMAs at all; without it, 70-100% of it does).
+// The sum of the 16-bit probabilities, which normalises O, is left to the matrix core:
+// one 16x16x32 product per P V step against a constant operand of ones (below), instead
+// of four VALU instructions per pair of scores.  (A v_dot2 per pair would wait for the
+// matrix core, which the other wave of the SIMD keeps busy in this schedule: measured on
+// gfx950, VALU work with one v_dot2 per pair of scores does not overlap another wave's
+// MFMAs at all; without it, 70-100% of it does.)
 // ----------------------------------------------------------------------------------
 template <class T, bool CAUSAL, int RING>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void fwd16_pp_kernel(
@@ -576,12 +578,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
   for (int st = 0; st < DS; ++st) qf[st] = buffer_load16(rq, qrow * (D * 2) + ((2 * st + half) << 4));
 
-  float m = -INFINITY, l = 0.f, lr = 0.f;
+  float m = -INFINITY, l = 0.f;
   f32x16 o[DB], s[KB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) s[kb] = (f32x16){};
+  // Sum of the 16-bit probabilities, on the matrix core: each P V step's B operand (16
+  // keys x 32 queries, lane l: query l % 32, 8 keys chosen by l / 32) also enters a
+  // 16x16x32 product, which reads it as 32 "keys" x 16 columns: lane l gives column l % 16
+  // and the contraction group l / 16, so column j mixes queries j (groups 0, 2) and j + 16
+  // (groups 1, 3).  Output (i, j) lands in lane j + 16 (i / 4).  The A operand (lane l:
+  // row l % 16, group l / 16) puts ones on groups 0 and 2 in rows i with i / 4 even and on
+  // groups 1 and 3 in rows with i / 4 odd, so that every output register of lane l holds
+  // the sum of query l % 32, the lane's own row: the rescale below multiplies it by the
+  // lane's own factor, like the accumulators of O.
+  const u32x4 ones = [&] {
+    const bool on = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1);
+    const uint32_t w = on ? T::kOnePair : 0u;
+    return (u32x4){w, w, w, w};
+  }();
+  f32x4 lsum = (f32x4){};
 
   // Product i < NPV is P V step i / DB of output block i % DB; product NPV + j is score
   // step j / KB of key block j % KB.
@@ -617,6 +634,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           const u32x4 b = (u32x4){__float_as_uint(s[kb][4 * mm]), __float_as_uint(s[kb][4 * mm + 1]),
                                   __float_as_uint(s[kb][4 * mm + 2]), __float_as_uint(s[kb][4 * mm + 3])};
           o[db] = T::mfma(a, b, o[db]);
+          if (db == DB - 1) lsum = T::mfma16(ones, b, lsum);
         } else {
           const int j = i - NPV, st = j / KB, kb = j % KB;
           s[kb] = T::mfma(a, qf[st], st == 0 ? (f32x16){} : s[kb]);
@@ -629,7 +647,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       __builtin_amdgcn_sched_group_barrier(0x100, FIRST, 0);
 #pragma unroll
       for (int i = I0; i < I0 + N; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < NPV && i % DB == DB - 1)
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // with the sum's product
+        else
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (i + RING < I0 + N) __builtin_amdgcn_sched_group_barrier(0x100, I0 < NPV ? 2 : 1, 0);
       }
     };
@@ -684,13 +705,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       const float m_new = fmaxf(m, mx);
       const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m - m_new);  // o, l are 0 while m = -inf
       l *= alpha;
-      lr *= alpha;
+      lsum *= alpha;  // the P V products of the tiles so far are all in (none is pending)
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] *= alpha;
       m = m_new;
     }
     const float mu = (m == -INFINITY) ? 0.f : m;  // every score of such a row is -inf: p = 0
-    float rs = 0.f, rsr = 0.f;
+    float rs = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -698,13 +719,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const float p0 = fast_exp2(fmaf(s[kb][2 * t2], c, -mu));
         const float p1 = fast_exp2(fmaf(s[kb][2 * t2 + 1], c, -mu));
         rs += p0 + p1;
-        const uint32_t pk = T::pack(p0, p1);
-        rsr += T::lo_f32(pk) + T::hi_f32(pk);
-        s[kb][t2] = __uint_as_float(pk);
+        s[kb][t2] = __uint_as_float(T::pack(p0, p1));
         if (t2 % 4 == 0) vfill(t, 2 * kb + t2 / 4);
       }
     l += rs;
-    lr += rsr;
   };
 
   // Q, K_0 (and V_0) have landed; the wait also settles the compiler's count of the Q
@@ -726,7 +744,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   wait_vmem();  // no fill may outlive the workgroup's LDS
   const float lt = sum_halves(l);
-  const float ltr = sum_halves(lr);
+  const float ltr = lsum[0];
   if (qrow >= R) return;
   const float inv = ltr > 0.f ? 1.0f / ltr : 0.f;
   uint16_t* orow = P.O + head + (size_t)qrow * D;

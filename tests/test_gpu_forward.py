@@ -43,6 +43,24 @@ def test_small_shapes_all_rows(dtype, d, causal):
               f"lse rel {worst:.2e}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_outlier_rows_move_the_running_max(dtype, d, causal):
+    """5% of the Q and K rows scaled by 8 (as in the large-head workload): scores reach
+    hundreds in log2 units, so the running max of a row jumps by very different amounts
+    from one key tile to the next, and the lazy rescale fires with a different factor on
+    every row.  All rows of all heads against the oracle."""
+    for n in (300, 700, 1100):
+        inp = make_inputs(1, 2, n, d, dtype, seed_base=7500 + n + d, outlier_frac=0.05, outlier_scale=8.0)
+        o, lse = run_fwd(inp, causal)
+        o_ref, lse_ref = naive.forward(to64(inp["q"]), to64(inp["k"]), to64(inp["v"]), 1 / math.sqrt(d), causal)
+        mx, mean, ex, _ = assert_close(f"O n={n}", o, o_ref, dtype, floor_aware=True)
+        worst = assert_lse(lse, lse_ref)
+        print(f"{dtype} d={d} causal={causal} N={n} outliers: O max {mx:.2e} (beyond floor {ex:.2e}) "
+              f"mean {mean:.2e} lse rel {worst:.2e}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_worked_examples_through_the_kernel(dtype):
     """The page examples embedded in a d = 64 head, scale 1, non-causal: softmax of
