@@ -110,6 +110,22 @@ struct f16_t {
   }
 };
 
+// Constant A operand that turns a 16x16x32 MFMA into per-query sums of a P V step's B
+// operand.  That operand (16 keys x 32 queries for v_mfma_f32_32x32x16: lane l holds query
+// l % 32 and 8 of the keys, chosen by l / 32) is read by the 16x16x32 product as 32
+// "keys" x 16 columns: lane l gives column l % 16 and contraction group l / 16, so column
+// j mixes queries j (groups 0, 2) and j + 16 (groups 1, 3).  Output (i, j) lands in lane
+// j + 16 (i / 4).  With ones on groups 0 and 2 in the rows i whose i / 4 is even and on
+// groups 1 and 3 in the others (lane l of A: row l % 16, group l / 16), all four output
+// registers of lane l hold the sum over the step's 16 keys for query l % 32, the lane's
+// own row, so a rescale multiplies it by the lane's own factor like the O accumulators.
+template <class T>
+__device__ __forceinline__ u32x4 row_sum_operand(int lane) {
+  const bool on = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1);
+  const uint32_t w = on ? T::kOnePair : 0u;
+  return (u32x4){w, w, w, w};
+}
+
 // Two fp32 values as a 16-bit pair hi plus the 16-bit pair of what hi missed, so that
 // hi + lo carries about twice the input type's significand.  A product A (hi + lo),
 // done as two MFMAs, then rounds only what both halves together cannot represent.

@@ -250,14 +250,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 #pragma unroll
   for (int st = 0; st < DS; ++st) qf[st] = buffer_load16(rq, qrow * (D * 2) + ((2 * st + half) << 4));
 
-  // base-2 exponent reference m (of s*c); this half's running sums: l of the fp32
-  // probabilities (for the logsumexp) and lr of the same probabilities rounded to 16 bits
-  // (for O).  m stays -inf while every key seen so far is masked for the row (only
-  // possible in a split that starts past a row's last visible key).
+  // base-2 exponent reference m (of s*c); running sums: l (this half's keys) of the fp32
+  // probabilities, for the logsumexp, and the sum of the same probabilities rounded to 16
+  // bits, for O.  At d = 128 the rounded sum is taken on the matrix core beside the P V
+  // products (lsum, row_sum_operand); at d = 64, where the kernel runs four waves per SIMD
+  // in 128 VGPRs, the 8 registers that takes spill, so there it is one v_dot2 per pair
+  // (lr, this half's keys).  m stays -inf while every key seen so far is masked for the
+  // row (only possible in a split that starts past a row's last visible key).
+  constexpr bool kMfmaSum = D == 128;
   float m = -INFINITY, l = 0.f, lr = 0.f;
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
+  const u32x4 ones = row_sum_operand<T>(lane);
+  f32x4 lsum = (f32x4){};
 
   for (int cur = 0; j < j1; cur ^= 1) {
     wait_vmem();
@@ -320,7 +326,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
             const float p1 = fast_exp2(fmaf(s[kb][2 * t2 + 1], c, -mu));
             rs += p0 + p1;
             pk[kb][t2] = T::pack(p0, p1);
-            rsr = T::sum2(pk[kb][t2], rsr);
+            if constexpr (!kMfmaSum) rsr = T::sum2(pk[kb][t2], rsr);
           }
       };
       bool move = __builtin_amdgcn_ballot_w64(m == -INFINITY) != 0;
@@ -339,6 +345,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m - m_new);  // o, l are 0 while m = -inf
         l *= alpha;
         lr *= alpha;
+        lsum *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db] *= alpha;
         m = m_new;
@@ -362,6 +369,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
         const float alpha = (m_new == -INFINITY) ? 1.0f : fast_exp2(m - m_new);  // o, l are 0 while m = -inf
         l *= alpha;
         lr *= alpha;
+        lsum *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db] *= alpha;
         m = m_new;
@@ -376,24 +384,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
           const float p1 = fast_exp2(fmaf(s[kb][2 * t2 + 1], c, -mu));
           rs += p0 + p1;
           pk[kb][t2] = T::pack(p0, p1);
-          rsr = T::sum2(pk[kb][t2], rsr);
+          if constexpr (!kMfmaSum) rsr = T::sum2(pk[kb][t2], rsr);
         }
       l += rs;
       lr += rsr;
     }
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T, and the rounded sums
 #pragma unroll
     for (int ks = 0; ks < BC / 16; ++ks) {
       const int kb = ks >> 1, mm = ks & 1;
       const u32x4 b = (u32x4){pk[kb][4 * mm], pk[kb][4 * mm + 1], pk[kb][4 * mm + 2], pk[kb][4 * mm + 3]};
 #pragma unroll
       for (int db = 0; db < DB; ++db) o[db] = T::mfma(lds_colop<D>(vt, 16 * ks, 32 * db, lane), b, o[db]);
+      if constexpr (kMfmaSum) lsum = T::mfma16(ones, b, lsum);
     }
   }
 
   const float lt = sum_halves(l);
-  const float ltr = sum_halves(lr);
+  const float ltr = kMfmaSum ? lsum[0] : sum_halves(lr);
   if (qrow >= R) return;
   if (SPLIT) {
     // partial result of this split: unnormalised o (fp32), the exponent reference m and
@@ -584,20 +593,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) s[kb] = (f32x16){};
-  // Sum of the 16-bit probabilities, on the matrix core: each P V step's B operand (16
-  // keys x 32 queries, lane l: query l % 32, 8 keys chosen by l / 32) also enters a
-  // 16x16x32 product, which reads it as 32 "keys" x 16 columns: lane l gives column l % 16
-  // and the contraction group l / 16, so column j mixes queries j (groups 0, 2) and j + 16
-  // (groups 1, 3).  Output (i, j) lands in lane j + 16 (i / 4).  The A operand (lane l:
-  // row l % 16, group l / 16) puts ones on groups 0 and 2 in rows i with i / 4 even and on
-  // groups 1 and 3 in rows with i / 4 odd, so that every output register of lane l holds
-  // the sum of query l % 32, the lane's own row: the rescale below multiplies it by the
-  // lane's own factor, like the accumulators of O.
-  const u32x4 ones = [&] {
-    const bool on = (((lane & 15) >> 2) & 1) == ((lane >> 4) & 1);
-    const uint32_t w = on ? T::kOnePair : 0u;
-    return (u32x4){w, w, w, w};
-  }();
+  // sum of the 16-bit probabilities, on the matrix core (row_sum_operand)
+  const u32x4 ones = row_sum_operand<T>(lane);
   f32x4 lsum = (f32x4){};
 
   // Product i < NPV is P V step i / DB of output block i % DB; product NPV + j is score
