@@ -446,14 +446,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
 }
 
 
-// LDS reads that fill the first `ring` slots of the two-phase kernel's operand ring: two
-// per P V operand (the first npv products), one per score operand.
-constexpr int pp_first_reads(int ring, int npv) {
-  int n = 0;
-  for (int i = 0; i < ring; ++i) n += i < npv ? 2 : 1;
-  return n;
-}
-
 // ----------------------------------------------------------------------------------
 // Two-phase schedule at d = 128 (no block mask, no split).  The hardware places waves w
 // and w + 4 of a workgroup on one SIMD, and a wave does not issue past its own MFMA while
@@ -482,10 +474,10 @@ constexpr int pp_first_reads(int ring, int npv) {
 // Each product's LDS operand is read RING products ahead into a register ring, so the
 // product phase does not wait on LDS with no second wave to cover the wait.  LDS
 // addresses are per-lane offsets held in registers plus constants; bit 15 of each offset
-// selects the buffer and flips after every product phase.  The first product phase
-// multiplies P = 0 by a zeroed V buffer, a wave's tiles past its last visible one get
-// P = 0, and the last phase's scores are discarded, so that every product phase runs the
-// same code.
+// selects the buffer and flips after every product phase.  A product phase runs its P V
+// half only for a tile the wave's rows see (so never in the first phase, which has no P
+// yet) and its score half only for such a tile (so never in the last); the offsets flip
+// either way, so that each phase addresses the buffers of its tile.
 //
 // The sum of the 16-bit probabilities, which normalises O, is left to the matrix core:
 // one 16x16x32 product per P V step against a constant operand of ones (below), instead
@@ -540,8 +532,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const uint16_t* fsrc = (grp == 1 ? P.K : P.V) + kvhead;
   const int fbuf0 = grp == 1 ? 0 : 2;
 
-  // Per-lane LDS offsets, for the buffers of the first product phase (K_0 in buffer 0,
-  // the zeroed V buffer 1).  Score operand of step st (key block kb adds kb * 32 rows):
+  // Per-lane LDS offsets, for the buffers of the first product phase (K_0 in buffer 0;
+  // V buffer 1, which that phase does not read).  Score operand of step st (key block kb adds kb * 32 rows):
   // row c32 of the K tile, chunk 2 st + half.  P V operand of output block db (step ks
   // adds 16 rows): the two transposing reads of lds_colop, rows r and r + 8.
   int koff[DS], voff[DB][2];
@@ -575,7 +567,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     return rsrc_words(base + (size_t)max(tile, 0) * BC * D, rem > 0 ? (uint32_t)rem : 0u);
   };
 
-  // prologue: K_0 (group B) and V_0 (group A), the zeros of V buffer 1, Q.  A block with
+  // prologue: K_0 (group B) and V_0 (group A), Q.  A block with
   // no key tile (only causal masking with Nq > Nk could make one; the library rejects
   // that shape) would skip the loop.
   if (NTL > 0) {
@@ -726,7 +718,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // loads, so that no wait for them is left inside the loop (where it would count the
   // fills in flight too)
   wait_vmem();
-  fa_sync();  // barrier 0: K_0, V_0 and the zeros are in LDS
+  fa_sync();  // barrier 0: K_0 and V_0 are in LDS
   for (int t = 0; t <= NTL && NTL > 0; ++t) {
     if (grp == 0) fa_sync();  // A: barrier 2t + 1
     products(t);
