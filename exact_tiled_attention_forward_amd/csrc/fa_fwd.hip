@@ -132,12 +132,17 @@ __device__ __forceinline__ bool rows_need_tile(const Fwd16Params& P, int bkv, in
 // method ("FlashAttention：IO 感知…", 基准/方法设计): with M = max_s m_s and
 // a_s = 2^(m_s - M), O = sum_s a_s o_s / sum_s a_s lr_s and lse = M + log2(sum_s a_s l_s)
 // (base 2, converted to natural log).  D / E lanes per row, E columns each (E = 4 for
-// the 256-row kernel's many rows, E = 2 for the few-row kernel's handful).
+// the 256-row kernel's many rows, E = 2 for the few-row kernel's handful).  The splits
+// are taken MC at a time: all loads of a chunk are issued together (one memory round
+// trip per chunk), then the chunk joins the running (M, sums) by the same rule.  With at
+// most MC splits there is one chunk, whose sums run in split order against the global M.
 template <class T, int D, int E, int BR, int BC, bool CAUSAL>
 __global__ __launch_bounds__(256) void fwd_merge_kernel(const Fwd16Params P) {
   static_assert(E == 2 || E == 4, "columns per lane");
+  typedef float fE __attribute__((ext_vector_type(E)));
   constexpr int LPR = D / E;      // lanes per row
   constexpr int RPB = 256 / LPR;  // rows per workgroup
+  constexpr int MC = 8;           // splits per chunk
   const int R = P.G * P.Nq;
   const size_t nrows = (size_t)P.BHkv * R;
   const size_t g = (size_t)blockIdx.x * RPB + threadIdx.x / LPR;
@@ -149,25 +154,43 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(const Fwd16Params P) {
   const float* pm = P.part + (size_t)P.nsplit * nrows * D;
   const float* pl = pm + (size_t)P.nsplit * nrows;
   const float* plr = pl + (size_t)P.nsplit * nrows;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, pm[s * nrows + g]);  // -inf only for a row with no visible key
+  float M = -INFINITY;  // stays -inf only for a row with no visible key
   float acc[E] = {};
   float lt = 0.f, lr = 0.f;
-#pragma unroll(E == 4 ? 4 : 1)
-  for (int s = 0; s < ns; ++s) {
-    const float ms = pm[s * nrows + g];
-    const float a = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
-    lt += a * pl[s * nrows + g];
-    lr += a * plr[s * nrows + g];
-    const float* po = P.part + (s * nrows + g) * D + c0;
-    if constexpr (E == 4) {
-      const f32x4 v = *(const f32x4*)po;
+  for (int s0 = 0; s0 < ns; s0 += MC) {
+    float ms[MC], ls[MC], lrs[MC];
+    fE os[MC];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] += a * v[e];
-    } else {
-      const f32x2 v = *(const f32x2*)po;
-      acc[0] += a * v[0];
-      acc[1] += a * v[1];
+    for (int k = 0; k < MC; ++k) {
+      const int s = s0 + k;
+      ms[k] = -INFINITY;
+      ls[k] = lrs[k] = 0.f;
+      os[k] = (fE){};
+      if (s < ns) {  // partials past the row's last split were not written
+        ms[k] = pm[s * nrows + g];
+        ls[k] = pl[s * nrows + g];
+        lrs[k] = plr[s * nrows + g];
+        os[k] = *(const fE*)(P.part + (s * nrows + g) * D + c0);
+      }
+    }
+    float Mc = M;
+#pragma unroll
+    for (int k = 0; k < MC; ++k) Mc = fmaxf(Mc, ms[k]);
+    if (Mc > M && M != -INFINITY) {  // a later chunk raised the max: rescale what is summed
+      const float f = fast_exp2(M - Mc);
+      lt *= f;
+      lr *= f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] *= f;
+    }
+    M = Mc;
+#pragma unroll
+    for (int k = 0; k < MC; ++k) {
+      const float a = (ms[k] == -INFINITY) ? 0.f : fast_exp2(ms[k] - M);
+      lt += a * ls[k];
+      lr += a * lrs[k];
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] += a * os[k][e];
     }
   }
   const float inv = lr > 0.f ? 1.0f / lr : 0.f;
