@@ -103,9 +103,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const uint8_t* mrow = SPARSE ? mask.bytes + (size_t)(bh % mask.Hq) * mask.hstride +
                                      (size_t)(q0 / kMaskBlock) * mask.nbk
                                : nullptr;
-  auto next_tile = [&](int j) {
-    if (SPARSE)
-      while (j < nkt && !mrow[(j * BC) / kMaskBlock]) ++j;
+  auto next_tile = [&](int j) {  // searched 64 tiles at a time, one tile per lane
+    if (SPARSE) {
+      for (; j < nkt; j += 64) {
+        const int jl = j + lane;
+        const uint64_t need = __builtin_amdgcn_ballot_w64(jl < nkt && mrow[(jl * BC) / kMaskBlock] != 0);
+        if (need != 0) return j + (int)__builtin_ctzll(need);
+      }
+      return nkt;
+    }
     return j;
   };
 
@@ -278,14 +284,21 @@ __global__ __launch_bounds__(2 * NP * 64) __attribute__((amdgpu_waves_per_eu(WPE
   // block-sparse: the workgroup's keys form one 128-key mask block, each query tile lies in
   // one 128-row block: hidden tiles are neither loaded nor computed
   static_assert(!SPARSE || (BKV == kMaskBlock && kMaskBlock % BQ == 0), "tiles inside mask blocks");
-  auto next_tile = [&](int t) {
+  auto next_tile = [&](int t) {  // searched 64 tiles at a time, one tile per lane
     if (SPARSE) {
       const int hbase = (bkv % (mask.Hq / G)) * G;  // the group's first query head within the batch
-      for (; t < ntiles; ++t) {
-        const int hq = hbase + t / nt;
-        const int qblk = ((qt0 + t % nt) * BQ) / kMaskBlock;
-        if (mask.bytes[(size_t)hq * mask.hstride + (size_t)qblk * mask.nbk + k0 / kMaskBlock]) break;
+      for (; t < ntiles; t += 64) {
+        const int tl = t + lane;
+        bool need = false;
+        if (tl < ntiles) {
+          const int hq = hbase + tl / nt;
+          const int qblk = ((qt0 + tl % nt) * BQ) / kMaskBlock;
+          need = mask.bytes[(size_t)hq * mask.hstride + (size_t)qblk * mask.nbk + k0 / kMaskBlock] != 0;
+        }
+        const uint64_t b = __builtin_amdgcn_ballot_w64(need);
+        if (b != 0) return t + (int)__builtin_ctzll(b);
       }
+      return ntiles;
     }
     return t;
   };

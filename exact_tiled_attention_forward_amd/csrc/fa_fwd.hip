@@ -248,11 +248,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const auto rk = make_rsrc(P.K + kvhead, (uint32_t)Nk * D * 2);
   const auto rv = make_rsrc(P.V + kvhead, (uint32_t)Nk * D * 2);
 
-  // block-sparse: tiles no row of the workgroup needs are neither loaded nor computed
+  // block-sparse: tiles no row of the workgroup needs are neither loaded nor computed.  The
+  // next needed tile is searched 64 tiles at a time, one tile per lane, so that a run of
+  // hidden tiles costs one round of mask reads instead of one read after another.
   const int rend = min(q0 + BR, R);
   auto next_tile = [&](int j) {
-    if (SPARSE)
-      while (j < j1 && !rows_need_tile<BC>(P, bkv, q0, rend, j)) ++j;
+    if (SPARSE) {
+      for (; j < j1; j += 64) {
+        const int jl = j + lane;
+        const uint64_t need = __builtin_amdgcn_ballot_w64(jl < j1 && rows_need_tile<BC>(P, bkv, q0, rend, jl));
+        if (need != 0) return j + (int)__builtin_ctzll(need);
+      }
+      return j1;
+    }
     return j;
   };
   // this lane's row of the mask (its query head and 128-row block)
@@ -291,19 +299,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   for (int cur = 0; j < j1; cur ^= 1) {
     wait_vmem();
     fa_sync();
+    const int k0 = j * BC;
+    // block-sparse: this lane's row keeps the tile's mask block.  Read and consumed (the
+    // ballot) before the next tile's fill is issued, so that waiting for this byte does not
+    // wait for the fill.
+    const bool lane_keep = SPARSE ? mrow[k0 / kMaskBlock] != 0 : true;
+    const uint64_t keep = SPARSE ? __builtin_amdgcn_ballot_w64(lane_keep) : ~0ull;
     const int jn = next_tile(j + 1);
     if (jn < j1) {
       tile_load_async<D, BC, NT>(lds + (cur ^ 1) * TB, rk, jn * BC, tid);
       tile_load_async<D, BC, NT>(lds + (2 + (cur ^ 1)) * TB, rv, jn * BC, tid);
     }
-    const int k0 = j * BC;
     j = jn;
     if (!wave_rows || (CAUSAL && k0 > wpmax + off)) continue;  // no row of the wave sees the tile
-    bool lane_keep = true;  // block-sparse: this lane's row keeps the tile's mask block
     bool mask_lanes = false;
     if (SPARSE) {
-      lane_keep = mrow[k0 / kMaskBlock] != 0;
-      const uint64_t keep = __builtin_amdgcn_ballot_w64(lane_keep);
       if (keep == 0) continue;
       mask_lanes = keep != ~0ull;
     }
