@@ -21,7 +21,9 @@
 //   * O^T += V^T P^T: P^T is the S^T accumulator converted to 16 bits in place (B
 //     operand); V^T is read from the row-major V tile with ds_read_b64_tr_b16.  Besides
 //     the fp32 row sum l (for the logsumexp), a second sum adds up the 16-bit
-//     probabilities the product actually used (v_dot2 with (1, 1)) and normalises O.
+//     probabilities the product actually used and normalises O: at d = 128 on the matrix
+//     core (a 16x16x32 product against a constant operand of ones, row_sum_operand), at
+//     d = 64 with one v_dot2 against (1, 1) per pair.
 //   * K/V tiles are fetched HBM -> LDS with buffer_load ... lds, double-buffered, so the
 //     next tile's fetch overlaps this tile's math.
 #include <algorithm>
@@ -45,8 +47,10 @@ namespace fa {
 // wave-uniform (one branch per tile) and after the first tiles of a row it is almost
 // never taken, which removes the multiply of every accumulator by alpha from the loop.
 //
-// Several waves share each SIMD (two at d = 128, four at d = 64), so while one wave's
-// MFMAs run another wave's softmax runs on the VALU.
+// Several waves share each SIMD (two at d = 128, four at d = 64).  Waves that run this
+// code in lock step multiply together and then exponentiate together; the two-phase
+// kernel below (d = 128 without a block mask or split) holds the two waves of a SIMD half
+// a tile apart, so that one's products run beside the other's softmax.
 // ----------------------------------------------------------------------------------
 constexpr float kRescaleSlack = 8.0f;
 // Products the two-phase kernel reads its LDS operands ahead of use.
