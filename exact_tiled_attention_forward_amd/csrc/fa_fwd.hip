@@ -300,6 +300,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
   const u32x4 ones = row_sum_operand<T>(lane);
   f32x4 lsum = (f32x4){};
 
+  // block-sparse masking: the lane's last visible key, less the 4 * half rows its
+  // accumulator layout adds
+  const int lane_lim = (SPARSE && D == 128) ? (CAUSAL ? min(pos + off, Nk - 1) : Nk - 1) - 4 * half : 0;
   for (int cur = 0; j < j1; cur ^= 1) {
     wait_vmem();
     fa_sync();
@@ -336,13 +339,25 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
     // masks: keys past the end, (causal) keys after the query's position, and
     // (block-sparse) rows whose mask block is 0
     if ((k0 + BC > Nk) || (CAUSAL && k0 + BC - 1 > wpmin + off) || mask_lanes) {
+      if constexpr (SPARSE && D == 128) {
+        // the key's offset in the tile, a constant per register, against the lane's last
+        // visible offset (-1: the lane's mask block is hidden): one compare per score.
+        // Block-masked d = 128 launches only: in the causal split kernel the same form
+        // spills (46 VGPRs at d = 64) and runs twice as long, and at d = 64 it spills too.
+        const int lim = lane_keep ? lane_lim - k0 : -1;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + 32 * kb + acc_row(i, half);
-          s[kb][i] = (!lane_keep || key >= Nk || (CAUSAL && key > pos + off)) ? -INFINITY : s[kb][i];
-        }
+          for (int i = 0; i < 16; ++i) s[kb][i] = 32 * kb + acc_row(i, 0) > lim ? -INFINITY : s[kb][i];
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + 32 * kb + acc_row(i, half);
+            s[kb][i] = (!lane_keep || key >= Nk || (CAUSAL && key > pos + off)) ? -INFINITY : s[kb][i];
+          }
+      }
     }
 
     // online softmax: exponentials, sums, 16-bit P
