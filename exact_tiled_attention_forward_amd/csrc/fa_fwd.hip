@@ -56,10 +56,16 @@ constexpr float kRescaleSlack = 8.0f;
 // Products the two-phase kernel reads its LDS operands ahead of use.
 constexpr int kPpRing = 6;
 // Largest sum of one lane's probabilities in a tile before the 256-row kernel at d = 64
-// moves its exponent reference: every probability then stays below 2^64, far from fp32
-// overflow.  Skipping the per-tile row max saves about a tenth of the softmax's vector
-// instructions (long non-causal d = 64 workload: 1.171 -> 1.127 ms).
+// moves its exponent reference.  The sum bounds every probability, and the P V product
+// takes each one in the input's 16-bit format: bf16 reaches about 2^128, so there the
+// bound is 2^64, far from fp32 overflow of o and l too; fp16 holds at most 65504, so there
+// it is 2^15 (a tile whose scores pass the reference by about 15 in log2 units moves it).
+// Skipping the per-tile row max saves about a tenth of the softmax's vector instructions
+// (long non-causal d = 64 workload: 1.171 -> 1.127 ms).
+template <class T>
 constexpr float kSumLimit = 18446744073709551616.0f;  // 2^64
+template <>
+constexpr float kSumLimit<f16_t> = 32768.0f;  // 2^15
 
 // Rows of the 16-bit kernel: the G*Nq query rows of one key/value head's group, packed.
 // The group's query heads are consecutive, so its rows are contiguous in Q and O, and
@@ -384,7 +390,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WP
       bool move = __builtin_amdgcn_ballot_w64(m == -INFINITY) != 0;
       if (!move) {
         exponentials(m);
-        move = __builtin_amdgcn_ballot_w64(!(rs <= kSumLimit)) != 0;
+        move = __builtin_amdgcn_ballot_w64(!(rs <= kSumLimit<T>)) != 0;
       }
       if (move) {
         float mx = -INFINITY;

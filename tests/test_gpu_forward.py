@@ -61,6 +61,38 @@ def test_outlier_rows_move_the_running_max(dtype, d, causal):
               f"mean {mean:.2e} lse rel {worst:.2e}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_scores_far_above_the_first_tile(dtype, d, causal):
+    """Two keys (300 and 301, past the first key tile of every kernel) whose scores lie 18 to
+    60 above every earlier score, in log2 units, with weights 4 : 1 or 2 : 1 between them.
+    A kernel that exponentiates against a stale reference would send their probabilities
+    past what the 16-bit P holds (fp16 stops at 65504) or flatten their ratio.  The shapes
+    run the 256-row kernel whole (16 heads of 1024) and split over the key range (2 heads
+    of 4096); every row against the oracle."""
+    cs = math.log2(math.e) / math.sqrt(d)  # score -> log2 units
+    for h, n in ((16, 1024), (2, 4096)):
+        for gaps in ((20.0, 18.0), (40.0, 39.0), (60.0, 58.0)):
+            g = torch.Generator().manual_seed(int(gaps[0]) + n + d)
+            q = 0.1 * torch.randn(1, h, n, d, generator=g)
+            k = 0.1 * torch.randn(1, h, n, d, generator=g)
+            v = torch.randn(1, h, n, d, generator=g)
+            q[..., 0] = 1.0
+            k[..., 0] = torch.linspace(-1.0, 1.0, n)
+            k[..., 300, 0] = gaps[0] / cs
+            k[..., 301, 0] = gaps[1] / cs
+            inp = {x: t.to(DT[dtype]) for x, t in (("q", q), ("k", k), ("v", v))}
+            o, lse = run_fwd(inp, causal)
+            assert not torch.isnan(o).any(), f"NaN in O ({h}x{n}, gaps {gaps})"
+            o_ref, lse_ref = naive.forward(to64(inp["q"]), to64(inp["k"]), to64(inp["v"]), 1 / math.sqrt(d),
+                                           causal)
+            mx, mean, ex, _ = assert_close(f"O {h}x{n} gaps {gaps}", o, o_ref, dtype, floor_aware=True)
+            worst = assert_lse(lse, lse_ref)
+            print(f"{dtype} d={d} causal={causal} {h}x{n} gaps {gaps}: O max {mx:.2e} (beyond floor {ex:.2e}) "
+                  f"lse rel {worst:.2e}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_worked_examples_through_the_kernel(dtype):
     """The page examples embedded in a d = 64 head, scale 1, non-causal: softmax of
