@@ -119,6 +119,10 @@ size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
  * D is summed from the recomputed fp32 P and dP rather than from the 16-bit o, and P
  * and dS enter the products as hi + lo 16-bit pairs; o is checked (non-NULL, aligned)
  * but its values are not read.  The result is deterministic (no atomics).
+ * With fp16 inputs both halves of dS are fp16, whose largest value is 65504, so every
+ * |dP_ij - D_i| must stay below it; d * max|dO| * max|V| < 32752 guarantees that.
+ * Larger values give non-finite gradients (no status reports it).  bf16 has no such
+ * limit short of fp32 overflow.
  * Equivalent to fa_backward_dq followed by fa_backward_dkdv on the same stream and
  * workspace.  Returns FA_OK or a negative fa_status_t.
  */
