@@ -93,6 +93,37 @@ def test_scores_far_above_the_first_tile(dtype, d, causal):
                   f"lse rel {worst:.2e}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("slope", [0.25, -0.25, 3.0], ids=["rising", "falling", "steep"])
+def test_monotone_scores_and_other_scales(dtype, d, slope):
+    """Scores that rise (or fall) steadily along the keys, by `slope` log2 units per key:
+    rising, every key tile passes the running max by 16 or more (the steep case by
+    hundreds), so each tile rescales o and both sums; falling, everything after the first
+    tile fades to nothing.  Run at three softmax scales (the default 1/sqrt(d), 1 and
+    1/64), causal and not, every row against the oracle."""
+    h, n = 4, 1024
+    g = torch.Generator().manual_seed(4000 + d + int(100 * slope))
+    q = 0.05 * torch.randn(1, h, n, d, generator=g)
+    k = 0.05 * torch.randn(1, h, n, d, generator=g)
+    v = torch.randn(1, h, n, d, generator=g)
+    for scale in (1 / math.sqrt(d), 1.0, 1 / 64):
+        cs = scale * math.log2(math.e)
+        qq, kk = q.clone(), k.clone()
+        # score of key j: 16 * k_j0 plus a little noise; the key values stay within fp16 range
+        qq[..., 0] = 16.0
+        kk[..., 0] = slope * (torch.arange(n, dtype=torch.float32) - n / 2) / (16.0 * cs)
+        inp = {x: t.to(DT[dtype]) for x, t in (("q", qq), ("k", kk), ("v", v))}
+        for causal in (False, True):
+            o, lse = run_fwd(inp, causal, scale=scale)
+            assert torch.isfinite(o).all(), f"non-finite O (scale {scale}, causal {causal})"
+            o_ref, lse_ref = naive.forward(to64(inp["q"]), to64(inp["k"]), to64(inp["v"]), scale, causal)
+            mx, mean, ex, _ = assert_close(f"O scale {scale} causal {causal}", o, o_ref, dtype, floor_aware=True)
+            worst = assert_lse(lse, lse_ref)
+            print(f"{dtype} d={d} slope {slope} scale {scale:.4f} causal={causal}: O max {mx:.2e} "
+                  f"(beyond floor {ex:.2e}) lse rel {worst:.2e}")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_worked_examples_through_the_kernel(dtype):
     """The page examples embedded in a d = 64 head, scale 1, non-causal: softmax of
