@@ -117,3 +117,55 @@ def test_values_beyond_fp16_range():
             assert e.max() <= 1e-2 * s and e.mean() <= 1e-3 * s, f"{where} {name}"
         if where is None:
             check_grads("after the large entries", tuple(g.cpu() for g in got), ref, "bf16")
+
+
+def _adversarial_scores(kind, h, n, d, dtype, seed):
+    """Q, K whose scores (log2 units at the default scale) either hold two keys 40 and 39
+    above every other score ("far") or rise by 0.75 per key ("steep", 48 per 64-key tile,
+    up to about 770 at the end); V and dO N(0,1)."""
+    g = torch.Generator().manual_seed(seed)
+    cs = math.log2(math.e) / math.sqrt(d)
+    q = 0.1 * torch.randn(1, h, n, d, generator=g)
+    k = 0.1 * torch.randn(1, h, n, d, generator=g)
+    v = torch.randn(1, h, n, d, generator=g)
+    do = torch.randn(1, h, n, d, generator=g)
+    if kind == "far":
+        q[..., 0] = 1.0
+        k[..., 0] = torch.linspace(-1.0, 1.0, n)
+        k[..., 300, 0] = 40.0 / cs
+        k[..., 301, 0] = 39.0 / cs
+    else:
+        q[..., 0] = 16.0
+        k[..., 0] = 0.75 * (torch.arange(n, dtype=torch.float32) - n / 2) / (16.0 * cs)
+    dt = {"f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    return {"q": q.to(dt), "k": k.to(dt), "v": v.to(dt), "do": do.to(dt)}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+@pytest.mark.parametrize("kind", ["far", "steep"])
+def test_far_and_steep_scores(kind, dtype, d, causal):
+    """The backward under scores far from the ordinary range: two keys 40 and 39 above every
+    other score, or scores rising by 0.75 (log2 units) per key.  P is recomputed from lse,
+    so the forward's lse must carry these rows exactly; most probabilities underflow to
+    zero and a few rows saturate on one key.  Keys in the hundreds make the gradients
+    large, so dO is first divided by the largest oracle gradient (the gradients are linear
+    in dO), which puts them at unit scale where the bar applies as written.
+    The slope stays moderate because dQ is ill-conditioned here: its terms dS_ij K_j cancel
+    (sum_j dS_ij = 0) against keys in the hundreds, and any fp32 kernel's lse, rounded at a
+    magnitude in the thousands, scales a row's P by 1 + 2^-13 or so and breaks that
+    cancellation.  At 3 per key (scores up to about 3000) a plain fp32 emulation on the CPU
+    already shows dQ errors of 2.4e-3 to 4.3e-3 against fp64, and the kernel, whose lse
+    carries the forward's few-ulp rounding, 5.6e-3 to 1.4e-2."""
+    h, n = 2, 1024
+    inp = _adversarial_scores(kind, h, n, d, dtype, seed=6100 + d)
+    q, k, v = (to64(inp[x]) for x in ("q", "k", "v"))
+    ref = naive.backward(q, k, v, to64(inp["do"]), 1 / math.sqrt(d), causal)
+    s = max(float(np.abs(r).max()) for r in ref)
+    inp["do"] = (inp["do"].float() / s).to(inp["do"].dtype)
+    ref = naive.backward(q, k, v, to64(inp["do"]), 1 / math.sqrt(d), causal)
+    got = run_fwd_bwd(inp, causal)
+    for name, gr in zip(("dQ", "dK", "dV"), got):
+        assert torch.isfinite(gr).all(), f"{name}: non-finite gradient"
+    print(f"{kind} {dtype} d={d} causal={causal} (dO / {s:.1f}): " + check_grads(kind, got, ref, dtype))
