@@ -11,7 +11,10 @@
 // not computed (same page, FlashAttention-2 section).
 //
 // Mapping to CDNA4 (one wave = 64 lanes owns 32 query rows):
-//   * o and l are rescaled only when a row's max moved by more than 8 in log2 units.
+//   * o and l are rescaled only when a row's exponent reference must move: when a
+//     tile's max passes it by more than 8 in log2 units, or, in the d = 64 kernel
+//     without a block mask, when a tile's probabilities against it add up to more than
+//     the 16-bit P can safely hold (kSumLimit).
 //   * S^T = K Q^T on v_mfma_f32_32x32x16: K (A operand) is read row-wise from LDS, Q (B
 //     operand) stays in registers for the whole kernel.  In the accumulator, lane l holds
 //     query l%32 and 16 of the tile's 32 keys, so the row max and row sum are in-lane
@@ -554,7 +557,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int DB = D / 32;           // 32-wide blocks of the output's head dimension
   constexpr int NPV = (BC / 16) * DB;  // P V products per tile
   constexpr int NSC = DS * KB;         // score products per tile
-  constexpr int NPR = NPV + NSC;
   constexpr int FPW = TB / (4 * 1024); // 1 KiB fills per wave of a group per tile
   static_assert(RING >= 1 && RING <= 7, "operand ring");
   static_assert(TB == 32768, "buffer parity is bit 15 of an LDS offset");
