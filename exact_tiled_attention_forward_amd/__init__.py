@@ -17,6 +17,7 @@ a cached K/V); see ``fa_forward``.
 from __future__ import annotations
 
 import ctypes
+import functools
 import math
 import os
 
@@ -123,6 +124,28 @@ def _gpu_tensor(name, t, dtype=None, shape=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _one_device(fn):
+    """Run an entry point with the device of its tensor arguments current, after checking
+    that they all live on that one device (a kernel launched on one GPU cannot read another
+    GPU's memory, and the no-workspace backward keeps its scratch per device)."""
+    @functools.wraps(fn)
+    def wrapped(*args, **kwargs):
+        tensors = [(f"argument {i}", a) for i, a in enumerate(args) if isinstance(a, torch.Tensor)]
+        tensors += [(k, a) for k, a in kwargs.items() if isinstance(a, torch.Tensor)]
+        gpu = [(name, t) for name, t in tensors if t.device.type == "cuda"]
+        if not gpu:
+            return fn(*args, **kwargs)  # the tensor checks report the CPU tensors
+        dev = gpu[0][1].device
+        for name, t in gpu:
+            if t.device != dev:
+                raise ValueError(f"{name} is on {t.device}, {gpu[0][0]} on {dev}: all tensors must be on one device")
+        if dev.index is None or dev.index == torch.cuda.current_device():
+            return fn(*args, **kwargs)
+        with torch.cuda.device(dev):
+            return fn(*args, **kwargs)
+    return wrapped
+
+
 def _stream(stream, device):
     s = torch.cuda.current_stream(device) if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -139,6 +162,7 @@ def _shapes(q, k):
     return B, Hq, Hkv, Nq, Nk, d
 
 
+@_one_device
 def fa_forward_split_count(q, k, causal=False):
     """The key-range split count the library suggests for these shapes (1: no split)."""
     B, Hq, Hkv, Nq, Nk, d = _shapes(q, k)
@@ -157,6 +181,7 @@ def _block_mask(block_mask, Hq, Nq, Nk):
     return _gpu_tensor("block_mask", block_mask, torch.uint8), int(block_mask.shape[0])
 
 
+@_one_device
 def fa_forward(q, k, v, o=None, lse=None, *, scale=None, causal=False, stream=None, split=None, workspace=None,
                block_mask=None):
     """O, lse = attention(q, k, v).
@@ -230,6 +255,7 @@ def _workspace(q, workspace):
     return workspace
 
 
+@_one_device
 def fa_backward(q, k, v, o, do, lse, dq=None, dk=None, dv=None, *, scale=None, causal=False,
                 workspace=None, stream=None, block_mask=None):
     """dQ (like q), dK, dV (like k) as float32 gradients of sum(O * dO), recomputing P from
@@ -264,6 +290,7 @@ def fa_backward(q, k, v, o, do, lse, dq=None, dk=None, dv=None, *, scale=None, c
     return dq, dk, dv
 
 
+@_one_device
 def fa_backward_noalloc(q, k, v, o, do, lse, dq, dk, dv, *, scale=None, causal=False, stream=None):
     """fa_backward without a workspace: the row statistics live in the library's static
     device scratch (at most 2^21 query rows B*Hq*Nq; see include/fa.h).  dq, dk, dv are
@@ -284,6 +311,7 @@ def fa_backward_noalloc(q, k, v, o, do, lse, dq, dk, dv, *, scale=None, causal=F
     return dq, dk, dv
 
 
+@_one_device
 def fa_backward_dq(q, k, v, do, lse, dq=None, *, scale=None, causal=False, workspace=None, stream=None):
     """First backward stage: dQ, plus D and lse*log2(e) in ``workspace`` (returned) for
     fa_backward_dkdv."""
@@ -307,6 +335,7 @@ def fa_backward_dq(q, k, v, do, lse, dq=None, *, scale=None, causal=False, works
     return dq, workspace
 
 
+@_one_device
 def fa_backward_dkdv(q, k, v, do, workspace, dk=None, dv=None, *, scale=None, causal=False, stream=None):
     """Second backward stage: dK, dV from the workspace fa_backward_dq filled."""
     lib = library()
@@ -331,6 +360,7 @@ def fa_backward_dkdv(q, k, v, do, workspace, dk=None, dv=None, *, scale=None, ca
     return dk, dv
 
 
+@_one_device
 def fa_quantize_fp8(x, *, per_channel=False, stream=None):
     """E4M3 codes (uint8, like x) and float32 scales of x (B, H, N, d): one scale per 128
     rows of a head, or per channel of a head with per_channel=True."""
@@ -348,6 +378,7 @@ def fa_quantize_fp8(x, *, per_channel=False, stream=None):
     return codes, scales
 
 
+@_one_device
 def fa_forward_fp8(q8, q_scale, k8, k_scale, v8, v_scale, o=None, lse=None, *, scale=None, causal=False,
                    stream=None):
     """O (bf16, like q8) and lse from E4M3 codes and their scales (see fa_quantize_fp8: row
