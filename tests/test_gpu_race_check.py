@@ -110,7 +110,10 @@ def test_backward_same_under_a_perturbed_schedule(case):
     both_builds(run)
 
 
-def test_block_sparse_same_under_a_perturbed_schedule():
+@pytest.mark.parametrize("split", [None, 1], ids=["library_split", "one_pass"])
+def test_block_sparse_same_under_a_perturbed_schedule(split):
+    """split=None lets this small grid split over the key range and merge the chunks;
+    split=1 keeps one pass over the needed tiles of each query block."""
     B, H, N, d = 1, 4, 1024, 128
     inp = make_cross_inputs(B, H, H, N, N, d, "bf16", seed_base=17000, with_do=True)
     q, k, v, do = (inp[x].cuda() for x in ("q", "k", "v", "do"))
@@ -119,7 +122,7 @@ def test_block_sparse_same_under_a_perturbed_schedule():
     mask = torch.from_numpy(m).cuda()
 
     def run():
-        o, lse = fa.fa_forward(q, k, v, block_mask=mask)
+        o, lse = fa.fa_forward(q, k, v, block_mask=mask, split=split)
         dq, dk, dv = fa.fa_backward(q, k, v, o, do, lse, block_mask=mask)
         return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
 

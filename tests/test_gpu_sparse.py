@@ -39,6 +39,13 @@ CASES = [
     (1, 4, 4, 640, 640, 128, "bf16", True, 4, 0.4, 3, None),
     (1, 2, 1, 1, 1000, 128, "bf16", True, 2, 0.5, None, None),
     (1, 2, 2, 260, 130, 64, "bf16", False, 2, 0.7, 1, 0),
+    # d = 128, lengths that are multiples of the mask block, one pass: grouped heads, Nq < Nk,
+    # an empty block row, a mask with no visible block at all, one that keeps everything
+    (1, 4, 2, 512, 640, 128, "bf16", False, 4, 0.5, 1, None),
+    (2, 4, 4, 768, 768, 128, "f16", True, 1, 0.5, 1, 3),
+    (1, 8, 2, 256, 1024, 128, "bf16", True, 8, 0.3, 1, None),
+    (1, 2, 1, 384, 384, 128, "bf16", False, 1, 0.0, 1, None),
+    (1, 2, 2, 1280, 1280, 128, "bf16", True, 2, 1.0, 1, None),
 ]
 
 
