@@ -94,3 +94,52 @@ def test_random_shape(case):
             gmx, gmean, _, _ = assert_close(f"{_id(case)} {name}", g.cpu(), r, dt, out_dtype="f32")
             msg += f"; {name} max {gmx:.2e}"
     print(_id(case) + ": " + msg)
+
+
+def _draw_fp8_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        Hkv = int(rng.integers(1, 3))
+        G = int(rng.choice([1, 2, 4]))
+        Nq, Nk = (int(np.exp(rng.uniform(0, np.log(1200)))) for _ in range(2))
+        causal = bool(rng.random() < 0.5)
+        if causal and Nq > Nk:
+            Nq, Nk = Nk, Nq
+        cases.append((i, int(rng.integers(1, 3)), Hkv * G, Hkv, Nq, Nk, d, causal))
+    return cases
+
+
+FP8_CASES = _draw_fp8_cases(24, seed=20240602)
+
+
+def _fp8_id(c):
+    i, B, Hq, Hkv, Nq, Nk, d, causal = c
+    return f"{i:02d}_B{B}_Hq{Hq}_Hkv{Hkv}_Nq{Nq}_Nk{Nk}_d{d}_{'causal' if causal else 'full'}"
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=[_fp8_id(c) for c in FP8_CASES])
+def test_random_shape_fp8(case):
+    """The E4M3 path on random shapes: quantize Q, K (128-row blocks) and V (channels),
+    then every element of O within the per-element bound derived for E4M3 probabilities,
+    fp32 arithmetic and the bf16 output, against exact attention on the dequantized
+    inputs; lse within its bound and the relative lse bar."""
+    from fp8_bound import forward_bound
+
+    i, B, Hq, Hkv, Nq, Nk, d, causal = case
+    inp = make_cross_inputs(B, Hq, Hkv, Nq, Nk, d, "bf16", seed_base=33000 + 41 * i)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    q8, qs = fa.fa_quantize_fp8(q)
+    k8, ks = fa.fa_quantize_fp8(k)
+    v8, vs = fa.fa_quantize_fp8(v, per_channel=True)
+    o, lse = fa.fa_forward_fp8(q8, qs, k8, ks, v8, vs, causal=causal)
+    torch.cuda.synchronize()
+    args = [a.cpu().numpy() for a in (q8, qs, k8, ks, v8, vs)]
+    o_ex, lse_ex, bound, lse_bound = forward_bound(*args, 1 / math.sqrt(d), causal)
+    err = np.abs(to64(o.cpu()) - o_ex)
+    assert (err <= bound).all(), f"{(err > bound).sum()} elements beyond the bound, worst excess {(err - bound).max():.3e}"
+    lse_out = to64(lse.cpu())
+    assert (np.abs(lse_out - lse_ex) <= lse_bound).all()
+    assert_lse(lse_out, lse_ex)
+    print(_fp8_id(case) + f": max {err.max():.2e}, max error/bound {(err / bound).max():.2f}")
